@@ -1,0 +1,206 @@
+"""Paged attention over a quantized (INT8 / packed INT4 / FP8 E4M3) KV cache
+for AMD MI355X (gfx950).
+
+A thin ctypes binding of the C ABI in include/paq.h: the functions below have
+the same names and arguments as the C entry points and only marshal them
+(device tensors -> data pointers, host arrays -> int32 buffers, the current
+torch stream -> hipStream_t).  Every step of the computation runs in the HIP
+kernels of libpaq.so; there is no Python or CPU fallback, and importing the
+functions fails loudly when the library has not been built
+(``python -m attention_paged_quantized_amd.build``).
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaq.so")
+
+PAQ_OK, PAQ_ERR_INVALID_ARG, PAQ_ERR_UNSUPPORTED, PAQ_ERR_WORKSPACE, PAQ_ERR_HIP = range(5)
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+KV_FORMATS = {"int8": 0, "int4": 1, "fp8": 2}
+SCALE_MODES = {"channel": 0, "head": 1}
+PATHS = {0: "none", 1: "single", 2: "split", 3: "f32_single", 4: "f32_split", 5: "prefill",
+         6: "f32_prefill"}
+
+# Every symbol include/paq.h declares.
+EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_decode",
+           "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
+           "paged_attn_prefill", "kv_quant_append")
+
+
+class PaqDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "token_count", "num_heads", "kv_num_heads", "head_size", "block_size",
+        "num_blocks", "max_blocks_per_seq", "q_dtype", "kv_format", "scale_mode")]
+
+
+class PaqPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_query_len", "max_kv_len", "active_seqs", "work_units", "num_splits", "path",
+        "grid_x", "grid_y", "grid_z", "reserved")] + [("workspace_bytes", ctypes.c_uint64)]
+
+
+class PaqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("paq status %d (%s): %s" % (status, status_string(status), message))
+        self.status = status
+
+
+_lib_handle = None
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_VP = ctypes.c_void_p
+
+
+def lib():
+    """The loaded libpaq.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libpaq.so is not built: run "
+                              "`python -m attention_paged_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.paq_abi_version.restype = ctypes.c_int32
+        L.paq_status_string.restype = ctypes.c_char_p
+        L.paq_status_string.argtypes = [ctypes.c_int32]
+        L.paq_last_error.restype = ctypes.c_char_p
+        L.paq_plan_decode.restype = ctypes.c_int32
+        L.paq_plan_decode.argtypes = [ctypes.POINTER(PaqDesc), _I32P, _I32P, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.POINTER(PaqPlan)]
+        L.paq_plan_prefill.restype = ctypes.c_int32
+        L.paq_plan_prefill.argtypes = [ctypes.POINTER(PaqDesc), _I32P, _I32P,
+                                       ctypes.POINTER(PaqPlan)]
+        L.paged_attn_decode_workspace_size.restype = ctypes.c_size_t
+        L.paged_attn_decode_workspace_size.argtypes = [ctypes.POINTER(PaqDesc), _I32P, _I32P,
+                                                       ctypes.c_int32]
+        attn = [ctypes.POINTER(PaqDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                _I32P, _I32P, ctypes.c_float]
+        L.paged_attn_decode.restype = ctypes.c_int32
+        L.paged_attn_decode.argtypes = attn + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
+        L.paged_attn_prefill.restype = ctypes.c_int32
+        L.paged_attn_prefill.argtypes = attn + [_VP]
+        L.kv_quant_append.restype = ctypes.c_int32
+        L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
+                                      _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
+        _lib_handle = L
+    return _lib_handle
+
+
+def status_string(status):
+    return lib().paq_status_string(int(status)).decode()
+
+
+def paq_status_string(status):
+    return status_string(status)
+
+
+def paq_last_error():
+    return lib().paq_last_error().decode()
+
+
+def paq_abi_version():
+    return int(lib().paq_abi_version())
+
+
+def make_desc(batch, token_count, num_heads, kv_num_heads, head_size, block_size, num_blocks,
+              max_blocks_per_seq, q_dtype, kv_format, scale_mode):
+    """A PaqDesc from Python values (dtype/format/mode names or enum ints)."""
+    def enum(v, table):
+        return table[v] if isinstance(v, str) else int(v)
+    return PaqDesc(int(batch), int(token_count), int(num_heads), int(kv_num_heads),
+                   int(head_size), int(block_size), int(num_blocks), int(max_blocks_per_seq),
+                   enum(q_dtype, DTYPES), enum(kv_format, KV_FORMATS),
+                   enum(scale_mode, SCALE_MODES))
+
+
+def _host_i32(a):
+    """Host int32 array -> (keepalive, pointer); None -> NULL."""
+    if a is None:
+        return None, None
+    if hasattr(a, "cpu") and hasattr(a, "numpy"):
+        a = a.cpu().numpy()
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_I32P)
+
+
+def _dev(t):
+    """Device tensor -> data pointer (None -> NULL)."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("expected a device (cuda/hip) tensor")
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return getattr(stream, "cuda_stream", stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status):
+    if status != PAQ_OK:
+        raise PaqError(status, paq_last_error())
+
+
+def paq_plan_decode(desc, cum_q_host, past_lens_host, num_splits=0, num_cus=0):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    plan = PaqPlan()
+    _check(lib().paq_plan_decode(ctypes.byref(desc), pa, pb, int(num_splits), int(num_cus),
+                                 ctypes.byref(plan)))
+    return plan
+
+
+def paq_plan_prefill(desc, cum_q_host, past_lens_host):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    plan = PaqPlan()
+    _check(lib().paq_plan_prefill(ctypes.byref(desc), pa, pb, ctypes.byref(plan)))
+    return plan
+
+
+def paged_attn_decode_workspace_size(desc, cum_q_host, past_lens_host, num_splits=0):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    return int(lib().paged_attn_decode_workspace_size(ctypes.byref(desc), pa, pb,
+                                                      int(num_splits)))
+
+
+def paged_attn_decode(desc, query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                      cum_q, past_lens, cum_q_host, past_lens_host, softmax_scale=0.0,
+                      num_splits=0, workspace=None, stream=None):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attn_decode(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        float(softmax_scale), int(num_splits), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_prefill(desc, query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                       cum_q, past_lens, cum_q_host, past_lens_host, softmax_scale=0.0,
+                       stream=None):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    _check(lib().paged_attn_prefill(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        float(softmax_scale), _stream(stream)))
+
+
+def kv_quant_append(desc, kv_in_dtype, key, value, key_cache, value_cache, k_scale, v_scale,
+                    block_table, cum_q, past_lens, cum_q_host, past_lens_host, stream=None):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    dt = DTYPES[kv_in_dtype] if isinstance(kv_in_dtype, str) else int(kv_in_dtype)
+    _check(lib().kv_quant_append(
+        ctypes.byref(desc), dt, _dev(key), _dev(value), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        _stream(stream)))

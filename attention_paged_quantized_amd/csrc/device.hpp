@@ -1,0 +1,134 @@
+// device.hpp -- gfx950 device helpers shared by the paged quantized-KV kernels:
+// element types, exact code->fp16/bf16 conversions, the E4M3 encoder, wave
+// reductions and the MFMA operand vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace paq {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { KV_INT8 = 0, KV_INT4 = 1, KV_FP8 = 2 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum { SCALE_CHANNEL = 0, SCALE_HEAD = 1 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int DT> struct dtype_of;
+template <> struct dtype_of<DT_F32> { typedef float type; };
+template <> struct dtype_of<DT_F16> { typedef f16 type; };
+template <> struct dtype_of<DT_BF16> { typedef bf16 type; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  // v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value {hi:lo}
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <typename T> __device__ __forceinline__ T bitcast(uint32_t x) {
+  return __builtin_bit_cast(T, x);
+}
+
+// ---------------------------------------------------------------------------
+// Quantization (bit contract of kv_quant_append).
+// ---------------------------------------------------------------------------
+
+// Round-half-even of an fp32 value to an integer code, clamped to [-m, m].
+__device__ __forceinline__ int quant_int(float q, float m) {
+  float r = __builtin_rintf(q);
+  r = fminf(fmaxf(r, -m), m);
+  return (int)r;
+}
+
+// OCP E4M3 encode with round-half-even and saturation to +-448.  Exact bit
+// manipulation of the fp32 input (NaN inputs are outside the contract).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  uint32_t u = __builtin_bit_cast(uint32_t, y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43E80000u) {            // |y| >= 464 (or inf): rounds past 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {      // |y| < 2^-6: subnormal grid, step 2^-9
+    float s = __builtin_bit_cast(float, a) * 512.0f;   // exact scaling
+    code = (uint32_t)__builtin_rintf(s);              // 0..8 (8 = smallest normal)
+  } else {                            // normal: keep 3 of 23 mantissa bits, RNE
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);   // rebias exponent 127 -> 7
+  }
+  return sign | code;
+}
+
+// OCP E4M3 code -> fp32 (exact): normal values rebias the exponent 7 -> 127,
+// subnormals are m * 2^-9.  NaN codes are never produced by the quantizer.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  const float mag = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20))
+                      : (float)m * 0x1p-9f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// Exact code -> fp16 conversions ("magic number" construction: the fp16 value
+// with exponent field 25 (0x6400 = 1024.0) has unit spacing, so placing an
+// unsigned integer u < 1024 in its mantissa bits gives exactly 1024 + u).
+// ---------------------------------------------------------------------------
+
+// Two signed bytes (already XOR-ed with 0x80, so u = code + 128) selected by
+// `sel` -> fp16 pair (code0, code1).  sel picks bytes of x into bytes 0 and 2.
+__device__ __forceinline__ f16x2 i8pair_to_f16x2(uint32_t x_biased, uint32_t sel02) {
+  uint32_t m = perm(0x64646464u, x_biased, sel02);
+  f16x2 v = bitcast<f16x2>(m);
+  return v - (f16x2){(f16)1152.0f, (f16)1152.0f};
+}
+
+// Nibbles (already XOR-ed with 0x8, so u = code + 8) at bits [0,4) and
+// [16,20) of x >> shift -> fp16 pair.
+__device__ __forceinline__ f16x2 nib_to_f16x2(uint32_t x_biased, int shift) {
+  uint32_t m = ((x_biased >> shift) & 0x000F000Fu) | 0x64006400u;
+  f16x2 v = bitcast<f16x2>(m);
+  return v - (f16x2){(f16)1032.0f, (f16)1032.0f};
+}
+
+// E4M3 bytes placed at bits [8,16) and [24,32) of y -> fp16 pair (exact):
+// the fp16 with bits sign<<15 | (code&0x7F)<<7 equals value * 2^-8.
+__device__ __forceinline__ f16x2 e4m3_hi_bytes_to_f16x2(uint32_t y) {
+  uint32_t m = (y & 0x80008000u) | ((y >> 1) & 0x3F803F80u);
+  f16x2 v = bitcast<f16x2>(m);
+  return v * (f16x2){(f16)256.0f, (f16)256.0f};
+}
+
+// ---------------------------------------------------------------------------
+// Wave (64-lane) reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace paq

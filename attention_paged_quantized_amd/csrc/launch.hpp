@@ -1,0 +1,57 @@
+// launch.hpp -- internal interface between the host library (paq_host.cpp) and
+// the kernel translation units.  Every launcher assumes the host has already
+// validated its arguments; it returns 0, or -1 for a format/dtype/shape
+// combination it was not built for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace paq {
+
+struct AppendArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* cum_q;
+  const int32_t* past_lens;
+  int batch, hkv, head_size, block_size, max_blocks;
+  int kv_format, scale_mode, in_dtype;
+  int max_query_len;   // exact, from the host cum_q
+  int tokens_per_wg;
+};
+
+struct AttnArgs {
+  const void* query;
+  void* out;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* cum_q;
+  const int32_t* past_lens;
+  float* part_o;        // split-KV partial outputs [T][H][S][D] (fp32), or null
+  float* part_lse;      // split-KV partial log-sum-exps [T][H][S], or null
+  int batch, token_count, num_heads, hkv, head_size, block_size, max_blocks;
+  int q_dtype, kv_format, scale_mode;
+  int num_splits;       // 1 = single pass (no partials)
+  int max_query_len;    // exact, from the host cum_q
+  float softmax_scale;  // already resolved (> 0)
+};
+
+int launch_quant_append(const AppendArgs& a, hipStream_t st);
+int launch_decode_f32(const AttnArgs& a, hipStream_t st);     // any q_len (portable)
+int launch_decode_mfma(const AttnArgs& a, hipStream_t st);    // q_len in {0,1}
+int launch_combine(const AttnArgs& a, hipStream_t st);
+int launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
+
+// Shape support of the MFMA kernels (host checks before choosing a path).
+bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype);
+bool prefill_mfma_supports(int head_size, int group, int block_size, int q_dtype);
+
+}  // namespace paq

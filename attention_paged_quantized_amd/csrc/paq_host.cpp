@@ -1,0 +1,406 @@
+// paq_host.cpp -- the C ABI (include/paq.h): argument validation, host-side
+// planning and kernel dispatch.
+//
+// Every check runs before anything is launched, so a failed call writes
+// nothing (the pages ask for explicit checks on values that cross the host /
+// device boundary: "PagedAttention FA path: exact max_query_len", lessons).
+// The grid of every kernel is sized from the exact maximum query length read
+// from the host copy of cum_q (same page, section 1), never from
+// token_count - batch + 1, which undercounts (or goes negative) as soon as a
+// sequence has no new token.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include "../../include/paq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+struct SeqStats {
+  int max_q = 0;       // exact max_query_len
+  int max_kv = 0;      // over sequences with new rows
+  int active = 0;      // sequences with new rows
+};
+
+bool valid_block_size(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+// Shape/enum/host-array checks shared by all calls.
+int validate(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
+             SeqStats* st) {
+  if (!d) return fail(PAQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0) return fail(PAQ_ERR_INVALID_ARG, "batch %d < 0", d->batch);
+  if (d->token_count < 0) return fail(PAQ_ERR_INVALID_ARG, "token_count %d < 0", d->token_count);
+  if (d->num_heads < 1 || d->kv_num_heads < 1)
+    return fail(PAQ_ERR_INVALID_ARG, "num_heads %d / kv_num_heads %d must be >= 1",
+                d->num_heads, d->kv_num_heads);
+  if (d->num_heads % d->kv_num_heads)
+    return fail(PAQ_ERR_INVALID_ARG, "num_heads %d is not a multiple of kv_num_heads %d",
+                d->num_heads, d->kv_num_heads);
+  if (d->q_dtype < PAQ_DT_F32 || d->q_dtype > PAQ_DT_BF16)
+    return fail(PAQ_ERR_INVALID_ARG, "q_dtype %d unknown", d->q_dtype);
+  if (d->kv_format < PAQ_KV_INT8 || d->kv_format > PAQ_KV_FP8_E4M3)
+    return fail(PAQ_ERR_INVALID_ARG, "kv_format %d unknown", d->kv_format);
+  if (d->scale_mode < PAQ_SCALE_PER_CHANNEL || d->scale_mode > PAQ_SCALE_PER_HEAD)
+    return fail(PAQ_ERR_INVALID_ARG, "scale_mode %d unknown", d->scale_mode);
+  if (d->head_size != 64 && d->head_size != 128)
+    return fail(PAQ_ERR_UNSUPPORTED, "head_size %d not built (64, 128)", d->head_size);
+  if (!valid_block_size(d->block_size))
+    return fail(PAQ_ERR_UNSUPPORTED, "block_size %d not built (16, 32, 64, 128)", d->block_size);
+  if (d->num_blocks < 0 || d->max_blocks_per_seq < 0)
+    return fail(PAQ_ERR_INVALID_ARG, "num_blocks %d / max_blocks_per_seq %d < 0",
+                d->num_blocks, d->max_blocks_per_seq);
+  if (d->batch > 0 && (!cum_q_host || !past_host))
+    return fail(PAQ_ERR_INVALID_ARG, "cum_q_host / past_lens_host is NULL");
+  if (d->batch == 0) {
+    if (d->token_count != 0)
+      return fail(PAQ_ERR_INVALID_ARG, "batch 0 with token_count %d", d->token_count);
+    if (cum_q_host && cum_q_host[0] != 0)
+      return fail(PAQ_ERR_INVALID_ARG, "cum_q[0] = %d, expected 0", cum_q_host[0]);
+    return PAQ_OK;
+  }
+  if (cum_q_host[0] != 0) return fail(PAQ_ERR_INVALID_ARG, "cum_q[0] = %d, expected 0", cum_q_host[0]);
+  const long cap = (long)d->max_blocks_per_seq * d->block_size;
+  for (int b = 0; b < d->batch; ++b) {
+    const long q = (long)cum_q_host[b + 1] - cum_q_host[b];
+    if (q < 0)
+      return fail(PAQ_ERR_INVALID_ARG, "cum_q decreases at sequence %d (%d -> %d)", b,
+                  cum_q_host[b], cum_q_host[b + 1]);
+    if (past_host[b] < 0) return fail(PAQ_ERR_INVALID_ARG, "past_lens[%d] = %d < 0", b, past_host[b]);
+    const long kv = (long)past_host[b] + q;
+    if (kv > 0x7fffffffL) return fail(PAQ_ERR_INVALID_ARG, "sequence %d length overflows", b);
+    if (q > 0) {
+      if (kv > cap)
+        return fail(PAQ_ERR_INVALID_ARG,
+                    "sequence %d needs %ld blocks of %d tokens, block_table has %d", b,
+                    (kv + d->block_size - 1) / d->block_size, d->block_size,
+                    d->max_blocks_per_seq);
+      st->active++;
+      st->max_q = std::max<long>(st->max_q, q);
+      st->max_kv = std::max<long>(st->max_kv, kv);
+    }
+  }
+  if (cum_q_host[d->batch] != d->token_count)
+    return fail(PAQ_ERR_INVALID_ARG, "cum_q[batch] = %d but token_count = %d",
+                cum_q_host[d->batch], d->token_count);
+  if (st->active > 0 && d->num_blocks < 1)
+    return fail(PAQ_ERR_INVALID_ARG, "num_blocks is 0 but sequences have tokens");
+  return PAQ_OK;
+}
+
+int device_cu_count(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(PAQ_ERR_HIP, "hipGetDevice failed (no GPU?)");
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && cache[dev] > 0) { *out = cache[dev]; return PAQ_OK; }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return fail(PAQ_ERR_HIP, "cannot query the compute-unit count of device %d", dev);
+  if (dev < 64) cache[dev] = n;
+  *out = n;
+  return PAQ_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
+                int num_splits, int num_cus, paq_plan* p) {
+  memset(p, 0, sizeof *p);
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_host, &st);
+  if (rc) return rc;
+  if (num_splits < 0) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d < 0", num_splits);
+  for (int b = 0; b < d->batch; ++b) {
+    const int q = cum_q_host[b + 1] - cum_q_host[b];
+    if (q > 1)
+      return fail(PAQ_ERR_INVALID_ARG,
+                  "decode needs q_len in {0,1}; sequence %d has %d new tokens", b, q);
+  }
+  p->max_query_len = st.max_q;
+  p->max_kv_len = st.max_kv;
+  p->active_seqs = st.active;
+  p->work_units = st.active * d->kv_num_heads;
+  if (st.active == 0) {
+    p->path = PAQ_PATH_NONE;
+    return PAQ_OK;
+  }
+  const int group = d->num_heads / d->kv_num_heads;
+  const bool mfma = d->q_dtype != PAQ_DT_F32 &&
+                    paq::decode_mfma_supports(d->head_size, group, d->block_size, d->q_dtype);
+  const int max_nb = (st.max_kv + d->block_size - 1) / d->block_size;
+  int S = num_splits;
+  if (S == 0) {
+    // Flash-decoding rule ("GQA GEMV decode", section 2): split the KV of a
+    // sequence only when the (sequence, kv head) units under-fill the device
+    // and a sequence has more than one KV chunk.  Aim at two workgroups per CU
+    // with chunks of at least 256 keys.
+    S = 1;
+    if (num_cus <= 0) {
+      rc = device_cu_count(&num_cus);
+      if (rc) return rc;
+    }
+    if (p->work_units < num_cus && max_nb > 1) {
+      const int want = (2 * num_cus + p->work_units - 1) / p->work_units;
+      const int by_len = std::max(1, st.max_kv / 256);
+      S = std::max(1, std::min(std::min(want, by_len), max_nb));
+    }
+  }
+  if (S > 4096) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d > 4096", S);
+  p->num_splits = S;
+  if (mfma) {
+    p->path = S > 1 ? PAQ_PATH_SPLIT : PAQ_PATH_SINGLE;
+    p->grid_x = d->kv_num_heads;
+    p->grid_y = d->batch;
+    p->grid_z = S;
+  } else {
+    p->path = S > 1 ? PAQ_PATH_F32_SPLIT : PAQ_PATH_F32_SINGLE;
+    p->grid_x = d->token_count;
+    p->grid_y = d->kv_num_heads;
+    p->grid_z = S;
+  }
+  if (S > 1) {
+    const size_t rows = (size_t)d->token_count * d->num_heads * S;
+    p->workspace_bytes = align_up(rows * d->head_size * sizeof(float)) + align_up(rows * sizeof(float));
+  }
+  return PAQ_OK;
+}
+
+int plan_prefill(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
+                 paq_plan* p) {
+  memset(p, 0, sizeof *p);
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_host, &st);
+  if (rc) return rc;
+  p->max_query_len = st.max_q;
+  p->max_kv_len = st.max_kv;
+  p->active_seqs = st.active;
+  p->work_units = st.active * d->kv_num_heads;
+  p->num_splits = 1;
+  if (st.max_q == 0) {
+    p->path = PAQ_PATH_NONE;          // nothing to launch (and no invalid grid)
+    return PAQ_OK;
+  }
+  const int group = d->num_heads / d->kv_num_heads;
+  if (d->q_dtype != PAQ_DT_F32 &&
+      paq::prefill_mfma_supports(d->head_size, group, d->block_size, d->q_dtype)) {
+    p->path = PAQ_PATH_PREFILL;
+    p->grid_x = 0;                     // filled by the launcher's tile size
+    p->grid_y = d->kv_num_heads;
+    p->grid_z = d->batch;
+  } else {
+    p->path = PAQ_PATH_F32_PREFILL;
+    p->grid_x = d->token_count;
+    p->grid_y = d->kv_num_heads;
+    p->grid_z = 1;
+  }
+  return PAQ_OK;
+}
+
+paq::AttnArgs attn_args(const paq_desc* d, const void* query, void* out, const void* kc,
+                        const void* vc, const float* ks, const float* vs, const int32_t* bt,
+                        const int32_t* cum_q, const int32_t* past, float softmax_scale,
+                        const paq_plan& p) {
+  paq::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.query = query;
+  a.out = out;
+  a.key_cache = (const uint8_t*)kc;
+  a.value_cache = (const uint8_t*)vc;
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.block_table = bt;
+  a.cum_q = cum_q;
+  a.past_lens = past;
+  a.batch = d->batch;
+  a.token_count = d->token_count;
+  a.num_heads = d->num_heads;
+  a.hkv = d->kv_num_heads;
+  a.head_size = d->head_size;
+  a.block_size = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.q_dtype = d->q_dtype;
+  a.kv_format = d->kv_format;
+  a.scale_mode = d->scale_mode;
+  a.num_splits = p.num_splits > 0 ? p.num_splits : 1;
+  a.max_query_len = p.max_query_len;
+  a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d->head_size);
+  return a;
+}
+
+int check_attn_pointers(const void* query, void* out, const void* kc, const void* vc,
+                        const float* ks, const float* vs, const int32_t* bt,
+                        const int32_t* cum_q, const int32_t* past) {
+  if (!query || !out || !kc || !vc || !ks || !vs || !bt || !cum_q || !past)
+    return fail(PAQ_ERR_INVALID_ARG, "a device pointer argument is NULL");
+  return PAQ_OK;
+}
+
+int launched(int launcher_rc, const char* what) {
+  if (launcher_rc != 0)
+    return fail(PAQ_ERR_UNSUPPORTED, "%s: no kernel built for this combination", what);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PAQ_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return PAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paq_abi_version(void) { return PAQ_ABI_VERSION; }
+
+const char* paq_status_string(int32_t s) {
+  switch (s) {
+    case PAQ_OK: return "ok";
+    case PAQ_ERR_INVALID_ARG: return "invalid argument";
+    case PAQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PAQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case PAQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* paq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t paq_plan_decode(const paq_desc* d, const int32_t* cum_q_host,
+                        const int32_t* past_lens_host, int32_t num_splits, int32_t num_cus,
+                        paq_plan* plan) {
+  if (!plan) return fail(PAQ_ERR_INVALID_ARG, "plan is NULL");
+  return plan_decode(d, cum_q_host, past_lens_host, num_splits, num_cus, plan);
+}
+
+int32_t paq_plan_prefill(const paq_desc* d, const int32_t* cum_q_host,
+                         const int32_t* past_lens_host, paq_plan* plan) {
+  if (!plan) return fail(PAQ_ERR_INVALID_ARG, "plan is NULL");
+  return plan_prefill(d, cum_q_host, past_lens_host, plan);
+}
+
+size_t paged_attn_decode_workspace_size(const paq_desc* d, const int32_t* cum_q_host,
+                                        const int32_t* past_lens_host, int32_t num_splits) {
+  paq_plan p;
+  if (plan_decode(d, cum_q_host, past_lens_host, num_splits, 0, &p) != PAQ_OK) return 0;
+  return (size_t)p.workspace_bytes;
+}
+
+int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
+                          const void* key_cache, const void* value_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* cum_q,
+                          const int32_t* past_lens, const int32_t* cum_q_host,
+                          const int32_t* past_lens_host, float softmax_scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  paq_plan p;
+  int rc = plan_decode(d, cum_q_host, past_lens_host, num_splits, 0, &p);
+  if (rc) return rc;
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  if (p.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+      return fail(PAQ_ERR_WORKSPACE, "split decode needs %llu workspace bytes, got %llu",
+                  (unsigned long long)p.workspace_bytes, (unsigned long long)workspace_bytes);
+    if (((uintptr_t)workspace) % 16)
+      return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, softmax_scale, p);
+  if (p.num_splits > 1) {
+    const size_t rows = (size_t)d->token_count * d->num_heads * p.num_splits;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT)
+    rc = launched(paq::launch_decode_mfma(a, st), "decode (MFMA)");
+  else
+    rc = launched(paq::launch_decode_f32(a, st), "decode (fp32)");
+  if (rc) return rc;
+  if (p.num_splits > 1) rc = launched(paq::launch_combine(a, st), "split-KV combine");
+  return rc;
+}
+
+int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
+                           const void* key_cache, const void* value_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* cum_q,
+                           const int32_t* past_lens, const int32_t* cum_q_host,
+                           const int32_t* past_lens_host, float softmax_scale,
+                           void* stream) {
+  paq_plan p;
+  int rc = plan_prefill(d, cum_q_host, past_lens_host, &p);
+  if (rc) return rc;
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, softmax_scale, p);
+  hipStream_t st = (hipStream_t)stream;
+  if (p.path == PAQ_PATH_PREFILL) return launched(paq::launch_prefill_mfma(a, st), "prefill (MFMA)");
+  return launched(paq::launch_decode_f32(a, st), "prefill (fp32)");
+}
+
+int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
+                        const void* value, void* key_cache, void* value_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* cum_q,
+                        const int32_t* past_lens, const int32_t* cum_q_host,
+                        const int32_t* past_lens_host, void* stream) {
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_lens_host, &st);
+  if (rc) return rc;
+  if (kv_in_dtype < PAQ_DT_F32 || kv_in_dtype > PAQ_DT_BF16)
+    return fail(PAQ_ERR_INVALID_ARG, "kv_in_dtype %d unknown", kv_in_dtype);
+  if (st.max_q == 0) return PAQ_OK;
+  if (!key || !value || !key_cache || !value_cache || !k_scale || !v_scale || !block_table ||
+      !cum_q || !past_lens)
+    return fail(PAQ_ERR_INVALID_ARG, "a device pointer argument is NULL");
+  paq::AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.cum_q = cum_q;
+  a.past_lens = past_lens;
+  a.batch = d->batch;
+  a.hkv = d->kv_num_heads;
+  a.head_size = d->head_size;
+  a.block_size = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.kv_format = d->kv_format;
+  a.scale_mode = d->scale_mode;
+  a.in_dtype = kv_in_dtype;
+  a.max_query_len = st.max_q;
+  const int chunks_per_tok = 2 * d->kv_num_heads * d->head_size / 8;
+  a.tokens_per_wg = std::max(1, 2048 / chunks_per_tok);
+  return launched(paq::launch_quant_append(a, (hipStream_t)stream), "kv_quant_append");
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host logic (validation, exact max_query_len, split planning,
+workspace sizing) behaves as documented.  No kernel is launched: every call
+here either fails validation or has nothing to launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import attention_paged_quantized_amd as paq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paq.h")
+FAKE = 0x10000          # a non-NULL "device" pointer that is never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = paq.lib()
+    names = _declared_functions()
+    assert sorted(names) == sorted(paq.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", paq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert paq.paq_abi_version() == 1
+    assert paq.paq_status_string(0) == "ok"
+    assert "workspace" in paq.paq_status_string(3)
+    assert paq.paq_status_string(99) == "unknown status"
+
+
+def _desc(B, T, H=32, hkv=8, D=128, bs=16, nb=100, mb=10, q="f16", fmt="int8", mode="channel"):
+    return paq.make_desc(B, T, H, hkv, D, bs, nb, mb, q, fmt, mode)
+
+
+def _cum(qlens):
+    return np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+
+
+def test_plan_decode_paths_and_workspace():
+    # tiny decode: fp32 queries -> the portable fp32 kernel, one pass
+    d = paq.make_desc(3, 2, 4, 2, 64, 16, 24, 8, "f32", "int8", "channel")
+    p = paq.paq_plan_decode(d, [0, 1, 2, 2], [37, 100, 0], 0, 256)
+    assert (p.max_query_len, p.max_kv_len, p.active_seqs, p.work_units) == (1, 101, 2, 4)
+    assert paq.PATHS[p.path] == "f32_single" or paq.PATHS[p.path] == "f32_split"
+    # long INT4 decode with 128 chunks: workspace = T*H*S*(D+1) fp32 (aligned)
+    d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
+    p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 128, 256)
+    assert p.num_splits == 128 and p.grid_z == 128
+    assert p.workspace_bytes == 4 * 32 * 128 * 128 * 4 + 4 * 32 * 128 * 4
+    assert paq.paged_attn_decode_workspace_size(d, _cum([1] * 4), [32768] * 4, 128) == \
+        p.workspace_bytes
+    # 256 (sequence, kv head) units fill 256 CUs: automatic choice is one pass
+    d = _desc(32, 32, mb=257, nb=6000)
+    p = paq.paq_plan_decode(d, _cum([1] * 32), [2000] * 32, 0, 256)
+    assert p.num_splits == 1 and p.workspace_bytes == 0
+    # 32 units under-fill 256 CUs and sequences are long: automatic split
+    d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
+    p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 0, 256)
+    assert p.num_splits == 16
+    # short sequences are not split
+    p = paq.paq_plan_decode(_desc(2, 2), _cum([1, 1]), [10, 100], 0, 256)
+    assert p.num_splits == 1
+
+
+def test_plan_prefill_uses_exact_max_query_len():
+    # q_lens {5,0,0}: the heuristic token_count-batch+1 would give 3
+    d = _desc(3, 5, mb=4)
+    p = paq.paq_plan_prefill(d, _cum([5, 0, 0]), [0, 7, 3])
+    assert p.max_query_len == 5 and p.active_seqs == 1
+    # {1,0,0,0}: the heuristic would be -2 (an invalid grid)
+    p = paq.paq_plan_prefill(_desc(4, 1, mb=4), _cum([1, 0, 0, 0]), [3, 0, 0, 0])
+    assert p.max_query_len == 1
+    # every sequence empty: nothing to launch
+    p = paq.paq_plan_prefill(_desc(3, 0, mb=4), _cum([0, 0, 0]), [5, 0, 2])
+    assert paq.PATHS[p.path] == "none"
+
+
+def _call_decode(d, cum, past, splits=1, ws=None, ws_bytes=0, ptr=FAKE):
+    L = paq.lib()
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    return L.paged_attn_decode(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                               pa, pb, 0.0, splits, ws, ws_bytes, None)
+
+
+def _call_prefill(d, cum, past, ptr=FAKE):
+    L = paq.lib()
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    return L.paged_attn_prefill(ctypes.byref(d), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                pa, pb, 0.0, None)
+
+
+def _call_append(d, cum, past, in_dtype=1, ptr=FAKE):
+    L = paq.lib()
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    return L.kv_quant_append(ctypes.byref(d), in_dtype, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                             ptr, pa, pb, None)
+
+
+BAD_CASES = [
+    # (description, desc kwargs, q_lens/cum, past, expected status)
+    ("cum_q decreases", dict(B=3, T=2), [0, 2, 1, 2], [1, 1, 1], paq.PAQ_ERR_INVALID_ARG),
+    ("cum_q[B] != token_count", dict(B=2, T=5), [0, 1, 2], [1, 1], paq.PAQ_ERR_INVALID_ARG),
+    ("cum_q[0] != 0", dict(B=2, T=2), [1, 1, 2], [1, 1], paq.PAQ_ERR_INVALID_ARG),
+    ("negative past", dict(B=2, T=2), [0, 1, 2], [1, -1], paq.PAQ_ERR_INVALID_ARG),
+    ("block table too short", dict(B=2, T=2, mb=2), [0, 1, 2], [31, 32],
+     paq.PAQ_ERR_INVALID_ARG),
+    ("H not a multiple of Hkv", dict(B=1, T=1, H=30), [0, 1], [4], paq.PAQ_ERR_INVALID_ARG),
+    ("head_size 96", dict(B=1, T=1, D=96), [0, 1], [4], paq.PAQ_ERR_UNSUPPORTED),
+    ("block_size 8", dict(B=1, T=1, bs=8), [0, 1], [4], paq.PAQ_ERR_UNSUPPORTED),
+    ("negative batch", dict(B=-1, T=0), [0], [0], paq.PAQ_ERR_INVALID_ARG),
+    ("no blocks but tokens", dict(B=1, T=1, nb=0), [0, 1], [4], paq.PAQ_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,cum,past,status", BAD_CASES, ids=[c[0] for c in BAD_CASES])
+def test_invalid_arguments_are_rejected_before_launch(name, kw, cum, past, status):
+    d = _desc(**kw)
+    assert _call_decode(d, cum, past) == status, paq.paq_last_error()
+    assert paq.paq_last_error()
+    assert _call_prefill(d, cum, past) == status
+    assert _call_append(d, cum, past) == status
+
+
+def test_decode_specific_checks():
+    d = _desc(2, 3)
+    assert _call_decode(d, [0, 2, 3], [4, 4]) == paq.PAQ_ERR_INVALID_ARG     # q_len 2
+    assert "q_len" in paq.paq_last_error()
+    assert _call_decode(_desc(1, 1), [0, 1], [4], splits=-1) == paq.PAQ_ERR_INVALID_ARG
+    # split decode without (or with too small) a workspace
+    assert _call_decode(_desc(1, 1), [0, 1], [100], splits=4) == paq.PAQ_ERR_WORKSPACE
+    assert _call_decode(_desc(1, 1), [0, 1], [100], splits=4, ws=FAKE, ws_bytes=64) == \
+        paq.PAQ_ERR_WORKSPACE
+    # NULL device pointers are caught once there is work
+    assert _call_decode(_desc(1, 1), [0, 1], [4], ptr=None) == paq.PAQ_ERR_INVALID_ARG
+
+
+def test_bad_enums_and_null_host_arrays():
+    assert _call_decode(_desc(1, 1, q="f16", fmt=7), [0, 1], [0]) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_decode(_desc(1, 1, mode=5), [0, 1], [0]) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_append(_desc(1, 1), [0, 1], [0], in_dtype=9) == paq.PAQ_ERR_INVALID_ARG
+    L = paq.lib()
+    d = _desc(1, 1)
+    assert L.paged_attn_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, None, None, 0.0, None) == paq.PAQ_ERR_INVALID_ARG
+
+
+def test_nothing_to_do_returns_ok_without_touching_the_device():
+    # zero-token step (every q_len 0): no launch, even with NULL device pointers
+    d = _desc(3, 0)
+    assert _call_decode(d, [0, 0, 0, 0], [5, 0, 9], ptr=None) == paq.PAQ_OK
+    assert _call_prefill(d, [0, 0, 0, 0], [5, 0, 9], ptr=None) == paq.PAQ_OK
+    assert _call_append(d, [0, 0, 0, 0], [5, 0, 9], ptr=None) == paq.PAQ_OK
+    # empty batch
+    d = _desc(0, 0)
+    assert _call_decode(d, [0], [], ptr=None) == paq.PAQ_OK
+    assert _call_prefill(d, [0], [], ptr=None) == paq.PAQ_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = _desc(1, 1)
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        paq.paged_attn_prefill(d, x, x, x, x, x, x, x, x, x, [0, 1], [0], stream=0)
