@@ -35,6 +35,8 @@ namespace paq {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecMaxGroup = 8;
+constexpr float kMaxSlack = 8.0f;          // lazy running-max slack (log2 units)
+constexpr float kPScale = 128.0f;          // fp16 P = p * 2^7, p <= 2^8 -> <= 2^15
 
 template <int KVF, int D> struct KvGeom {
   static constexpr int C = (KVF == KV_INT4) ? D / 2 : D;      // bytes per row
@@ -131,18 +133,97 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vw)[8][2], f16x8 (&v
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming through LDS.  Every wave owns a private ring of two tile slots.
+// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane
+// straight into LDS, no registers held while in flight), two tiles ahead of the
+// one being computed.  A slot holds the 32 K rows then the 32 V rows of one
+// tile, row-major; the 16-byte chunks of row r are stored XOR-swizzled by
+// (r mod chunks-per-row) so that the operand reads below are free of bank
+// conflicts.  The compiler does not track LDS-DMA completion, so the kernel
+// waits on vmcnt itself (in-order completion of vector memory loads).
+// ---------------------------------------------------------------------------
+template <int KVF, int D> struct Ring {
+  using Geo = KvGeom<KVF, D>;
+  static constexpr int C = Geo::C;
+  static constexpr int CH = C / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;           // rows per DMA instruction
+  static constexpr int NI = 32 / RPI;           // DMA instructions per 32 rows
+  static constexpr int SLOT = 64 * C;           // K rows + V rows
+};
+
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+  // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+// Queue the copy of the tile starting at key k0 into `slot` (wave-uniform).
+// Keys past the chunk end are clamped to its last key (a valid row).
+struct TileOffsets {
+  size_t off0, off1;   // byte offsets of the physical blocks of the two 16-key halves
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(int k0, int kend, int lbs,
+                                                    const int32_t* __restrict__ table,
+                                                    uint32_t row_stride) {
+  TileOffsets t;
+  t.off0 = ((size_t)table[min(k0, kend - 1) >> lbs] << lbs) * row_stride;
+  t.off1 = ((size_t)table[min(k0 + 16, kend - 1) >> lbs] << lbs) * row_stride;
+  return t;
+}
+
+template <int KVF, int D>
+__device__ __forceinline__ void issue_tile(uint8_t* slot, int k0, int kend, int lbs,
+                                           TileOffsets to, const uint8_t* kbase,
+                                           const uint8_t* vbase, uint32_t row_stride, int lane) {
+  using R = Ring<KVF, D>;
+  const int bmask = (1 << lbs) - 1;
+  const size_t off0 = to.off0, off1 = to.off1;
+  const int c = lane % R::CH;
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const int r = R::RPI * i + lane / R::CH;
+    const uint32_t row = (uint32_t)(min(k0 + r, kend - 1) & bmask);
+    const uint32_t lane_off = row * row_stride + 16u * (uint32_t)(c ^ (r % R::CH));
+    const size_t off = (r < 16) ? off0 : off1;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(kbase + off + lane_off),
+        (__attribute__((address_space(3))) void*)(slot + i * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < R::NI; ++i) {
+    const int r = R::RPI * i + lane / R::CH;
+    const uint32_t row = (uint32_t)(min(k0 + r, kend - 1) & bmask);
+    const uint32_t lane_off = row * row_stride + 16u * (uint32_t)(c ^ (r % R::CH));
+    const size_t off = (r < 16) ? off0 : off1;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(vbase + off + lane_off),
+        (__attribute__((address_space(3))) void*)(slot + 32 * R::C + i * 1024), 16, 0, 0);
+  }
+}
+
+// Byte offset of byte b of row r inside a K or V block of a slot.
+template <int KVF, int D>
+__device__ __forceinline__ int slot_off(int r, int b) {
+  using R = Ring<KVF, D>;
+  return r * R::C + 16 * ((b >> 4) ^ (r % R::CH)) + (b & 15);
+}
+
 template <int NB>
-__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
-  if constexpr (NB == 32) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
-    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
-    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
-  } else if constexpr (NB == 16) {
-    u32x4 a = *reinterpret_cast<const u32x4*>(p);
+__device__ __forceinline__ void lds_bytes(const uint8_t* p, uint32_t* w) {
+  if constexpr (NB == 16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
   } else if constexpr (NB == 8) {
-    u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
     w[0] = a[0]; w[1] = a[1];
   } else if constexpr (NB == 4) {
     w[0] = *reinterpret_cast<const uint32_t*>(p);
@@ -152,9 +233,107 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
   }
 }
 
-template <int D, int KVF, int SM, typename TQ>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(AttnArgs a) {
+// One tile's operand bytes for this lane, read from a slot.
+template <int KVF, int D> struct TileRaw {
+  uint32_t kw[2][KvGeom<KVF, D>::KDW];   // K: key col of each 16-key half, segment grp
+  uint32_t vw[8][2];                      // V: keys {4grp+r, 16+4grp+r}, channels (D/16)*col..
+};
+
+template <int KVF, int D>
+__device__ __forceinline__ void read_tile(const uint8_t* slot, TileRaw<KVF, D>& t, int col,
+                                          int grp) {
   using Geo = KvGeom<KVF, D>;
+  using R = Ring<KVF, D>;
+  constexpr int KB = Geo::KBYTES;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 16 * hh + col;
+    if constexpr (KB >= 16) {
+#pragma unroll
+      for (int j = 0; j < KB / 16; ++j)
+        lds_bytes<16>(slot + slot_off<KVF, D>(r, KB * grp + 16 * j), &t.kw[hh][4 * j]);
+    } else {
+      lds_bytes<KB>(slot + slot_off<KVF, D>(r, KB * grp), t.kw[hh]);
+    }
+  }
+  const uint8_t* vs = slot + 32 * R::C;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
+    t.vw[e][1] = 0;
+    lds_bytes<Geo::VBYTES>(vs + slot_off<KVF, D>(r, Geo::VBYTES * col), t.vw[e]);
+  }
+}
+
+// Per-wave online-softmax state: running max (log2 units), this lane's share of
+// the running sum, and the O^T accumulators (lane j+16q: query column j,
+// channels (D/16)*(4q+r) + nb).
+template <int D> struct WaveState {
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[D / 16];
+};
+
+template <int KVF, int D>
+__device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, int kend,
+                                             float c2, const f16x8 (&qhi)[D / 32],
+                                             const f16x8 (&qlo)[D / 32], WaveState<D>& st,
+                                             int grp) {
+  constexpr int NQK = D / 32, NPV = D / 16;
+  // S^T = K Q'^T (hi + lo); the two 16-key halves are independent chains
+  f32x4 s0 = (f32x4){0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+  for (int m = 0; m < NQK; ++m) {
+    const f16x8 k0op = k_operand<KVF, D>(t.kw[0], m);
+    const f16x8 k1op = k_operand<KVF, D>(t.kw[1], m);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0op, qhi[m], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1op, qhi[m], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0op, qlo[m], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1op, qlo[m], s1, 0, 0, 0);
+  }
+  // scale to log2 units, mask keys past the chunk
+  float v[8];
+  float lm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    v[r] = (k0 + 4 * grp + r < kend) ? s0[r] * c2 : -INFINITY;
+    v[4 + r] = (k0 + 16 + 4 * grp + r < kend) ? s1[r] * c2 : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lm = fmaxf(lm, v[i]);
+  // The reference maximum of a column is shared by its four lane rows and only
+  // moves when a score exceeds it by more than kMaxSlack (log2 units): then the
+  // rows exchange their maxima and the accumulators are rescaled.  Otherwise
+  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^kPScale-scaled fp16 P holds.
+  if (__ballot(lm > st.m + kMaxSlack)) {
+    const float m_new = fmaxf(st.m, rows_max(lm));
+    const float alpha = fast_exp2(st.m - m_new);         // 0 on the first update
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) st.o[i] *= alpha;
+  }
+  f16x8 pop;
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = fast_exp2(v[i] - st.m);
+    psum += p;
+    pop[i] = (f16)(p * kPScale);
+  }
+  st.l += psum;
+  // O^T += V^T P^T
+  f16x8 vop[NPV];
+  v_operands<KVF, D>(t.vw, vop);
+#pragma unroll
+  for (int nbk = 0; nbk < NPV; ++nbk)
+    st.o[nbk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[nbk], pop, st.o[nbk], 0, 0, 0);
+}
+
+template <int D, int KVF, int SM, typename TQ, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
+                                                             const int32_t* __restrict__ block_table) {
+  using Geo = KvGeom<KVF, D>;
+  using R = Ring<KVF, D>;
   constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
   const int h = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
   const int q0 = a.cum_q[b];
@@ -166,17 +345,50 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(AttnArgs a)
   const int S = a.num_splits;
   const int kbeg = (int)(((long)chunk * nb) / S) * bs;
   const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
+  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+  const int lbs = a.block_size_log2;
+  const uint32_t row_stride = (uint32_t)(hkv * C);         // bytes between tokens
+  const uint8_t* kbase = a.key_cache + (size_t)h * C;
+  const uint8_t* vbase = a.value_cache + (size_t)h * C;
+  constexpr int stride = 32 * NW;
+
+  constexpr int WAVE_BYTES = NS * R::SLOT;                 // NS slots per wave
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][WAVE_BYTES];
+  uint8_t* myring = ring[wave];
+
+  // start streaming this wave's first NS tiles before the set-up work
+  const int k_first = kbeg + 32 * wave;
+  if (kbeg < kend) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      issue_tile<KVF, D>(myring + j * R::SLOT, k_first + j * stride, kend, lbs,
+                         tile_offsets(k_first + j * stride, kend, lbs, table, row_stride), kbase,
+                         vbase, row_stride, lane);
+  }
 
   // ---- fold the key scale into the query: Q' = Q * s / M, split hi + lo ----
-  float smax = 0.f;
+  // lane (col, grp) holds query column col, channels [(D/4)*grp, (D/4)*(grp+1))
+  constexpr int SEG = D / 4;
+  float sv[SEG];
+  float smax;
   if constexpr (SM == SCALE_CHANNEL) {
-    for (int d = lane; d < D; d += 64) smax = fmaxf(smax, fabsf(a.k_scale[h * D + d]));
-    smax = wave_max(smax);
+    const f32x4* sp = reinterpret_cast<const f32x4*>(a.k_scale + h * D + SEG * grp);
+#pragma unroll
+    for (int i = 0; i < SEG / 4; ++i) {
+      const f32x4 x = sp[i];
+      sv[4 * i] = x[0]; sv[4 * i + 1] = x[1]; sv[4 * i + 2] = x[2]; sv[4 * i + 3] = x[3];
+    }
+    smax = 0.f;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) smax = fmaxf(smax, fabsf(sv[i]));
+    smax = rows_max(smax);
   } else {
     smax = fabsf(a.k_scale[h]);
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) sv[i] = a.k_scale[h];
   }
   int ex;
   const float fr = frexpf(smax, &ex);                      // smax = fr * 2^ex, fr in [0.5,1)
@@ -184,17 +396,26 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(AttnArgs a)
   const float invM = 1.f / Mh;                             // exact (power of two)
   f16x8 qhi[NQK], qlo[NQK];
   {
-    const TQ* q = reinterpret_cast<const TQ*>(a.query) + ((size_t)q0 * H + h * G + col) * D;
+    float qv[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) qv[i] = 0.f;
+    if (col < G) {
+      const TQ* q = reinterpret_cast<const TQ*>(a.query) + ((size_t)q0 * H + h * G + col) * D +
+                    SEG * grp;
+#pragma unroll
+      for (int i = 0; i < SEG / 8; ++i) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(q)[i];
+        const TQ* e = reinterpret_cast<const TQ*>(&x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[8 * i + j] = to_f32(e[j]);
+      }
+    }
 #pragma unroll
     for (int m = 0; m < NQK; ++m) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = 0.f;
-        if (col < G) {
-          const int ch = qk_channel<KVF, D>(grp, m, e);
-          const float s = (SM == SCALE_CHANNEL) ? a.k_scale[h * D + ch] : a.k_scale[h];
-          x = to_f32(q[ch]) * (s * invM);
-        }
+        const int c = qk_channel<KVF, D>(0, m, e);        // channel within the segment
+        const float x = qv[c] * (sv[c] * invM);
         const f16 hi = (f16)x;
         qhi[m][e] = hi;
         qlo[m][e] = (f16)(x - (float)hi);
@@ -203,121 +424,66 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(AttnArgs a)
   }
   const float c2 = a.softmax_scale * Mh * kLog2e;          // score -> log2 units
 
-  // ---- per-wave online softmax over this wave's 32-key tiles ----
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[NPV];
+  // ---- per-wave online softmax over this wave's tiles ----
+  WaveState<D> st;
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const size_t row_stride = (size_t)hkv * C;               // bytes between tokens
-  const uint8_t* kbase = a.key_cache + (size_t)h * C;
-  const uint8_t* vbase = a.value_cache + (size_t)h * C;
-
-  for (int k0 = kbeg + 32 * wave; k0 < kend; k0 += 32 * kDecWaves) {
-    // physical blocks of the two 16-key halves (clamped into the chunk)
-    const int kc0 = min(k0, kend - 1), kc1 = min(k0 + 16, kend - 1);
-    const size_t blk0 = (size_t)table[kc0 / bs], blk1 = (size_t)table[kc1 / bs];
-    // K rows: lane -> key (col) of each half, byte segment grp
-    uint32_t kw[2][Geo::KDW];
-    {
-      const int key0 = min(k0 + col, kend - 1), key1 = min(k0 + 16 + col, kend - 1);
-      const uint8_t* p0 = kbase + (blk0 * bs + key0 % bs) * row_stride + Geo::KBYTES * grp;
-      const uint8_t* p1 = kbase + (blk1 * bs + key1 % bs) * row_stride + Geo::KBYTES * grp;
-      load_bytes<Geo::KBYTES>(p0, kw[0]);
-      load_bytes<Geo::KBYTES>(p1, kw[1]);
+  for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (kbeg < kend) {
+    int cur = 0;
+    // block offsets of the tile issued next, fetched one iteration early
+    TileOffsets nxt = tile_offsets(k_first + NS * stride, kend, lbs, table, row_stride);
+    for (int k = k_first; k < kend; k += stride) {
+      // this tile's copies are done once at most the later tiles' remain
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_le((NS - 1) * 2 * R::NI);
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* slot = myring + cur * R::SLOT;
+      TileRaw<KVF, D> t;
+      read_tile<KVF, D>(slot, t, col, grp);
+      // the slot is refilled (NS tiles ahead) once every lane has read it
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      issue_tile<KVF, D>(slot, k + NS * stride, kend, lbs, nxt, kbase, vbase, row_stride, lane);
+      nxt = tile_offsets(k + (NS + 1) * stride, kend, lbs, table, row_stride);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<KVF, D>(t, k, kend, c2, qhi, qlo, st, grp);
+      cur = (cur + 1 == NS) ? 0 : cur + 1;
     }
-    // V rows: lane (dd, grp) -> keys {4grp+r, 16+4grp+r}, channels (D/16)*dd..
-    uint32_t vw[8][2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = min(k0 + (e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4)), kend - 1);
-      const size_t blk = e < 4 ? blk0 : blk1;
-      const uint8_t* p = vbase + (blk * bs + key % bs) * row_stride + Geo::VBYTES * col;
-      vw[e][1] = 0;
-      load_bytes<Geo::VBYTES>(p, vw[e]);
-    }
-    // S^T = K Q'^T (hi + lo)
-    f32x4 s[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < NQK; ++m) {
-        const f16x8 kop = k_operand<KVF, D>(kw[hh], m);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qhi[m], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qlo[m], acc, 0, 0, 0);
-      }
-      s[hh] = acc;
-    }
-    // scale, mask, tile maximum per query column
-    float mt = -INFINITY;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 16 * hh + 4 * grp + r;
-        const float v = key < kend ? s[hh][r] * c2 : -INFINITY;
-        s[hh][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);          // 0 on the first tile
-    m_run = m_new;
-    f16x8 pop;
-    float psum = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(s[hh][r] - m_new);
-        psum += p;
-        pop[4 * hh + r] = (f16)(p * 32768.0f);
-      }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) o[i] *= alpha;
-    }
-    // O^T += V^T P^T
-    f16x8 vop[NPV];
-    v_operands<KVF, D>(vw, vop);
-#pragma unroll
-    for (int nbk = 0; nbk < NPV; ++nbk)
-      o[nbk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[nbk], pop, o[nbk], 0, 0, 0);
   }
+  // drain this wave's outstanding copies before its ring is reused below
+  wait_vmcnt_le(0);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- merge the waves through LDS ----
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  __shared__ float sm_m[kDecWaves][kDecMaxGroup], sm_l[kDecWaves][kDecMaxGroup];
-  __shared__ float sm_o[kDecWaves][kDecMaxGroup][D];
+  // ---- merge the waves through LDS (each wave writes into its own ring) ----
+  const float l_run = rows_sum(st.l);
+  __shared__ float sm_ml[NW][2][kDecMaxGroup];             // running max, sum per wave
+  float* wo = reinterpret_cast<float*>(myring);             // [kDecMaxGroup][D] per wave
+  static_assert(kDecMaxGroup * D * 4 <= WAVE_BYTES, "merge area");
   if (col < G) {
-    if (grp == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }
+    if (grp == 0) { sm_ml[wave][0][col] = st.m; sm_ml[wave][1][col] = l_run; }
 #pragma unroll
     for (int nbk = 0; nbk < NPV; ++nbk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[wave][col][(D / 16) * (4 * grp + r) + nbk] = o[nbk][r];
+      for (int r = 0; r < 4; ++r) wo[col * D + (D / 16) * (4 * grp + r) + nbk] = st.o[nbk][r];
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += kDecWaves * 64) {
+  for (int t = threadIdx.x; t < G * D; t += NW * 64) {
     const int cq = t / D, d = t % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm_m[w][cq]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][0][cq]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float f = fast_exp2(sm_m[w][cq] - M);
-        L += f * sm_l[w][cq];
-        O += f * sm_o[w][cq][d];
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(sm_ml[w][0][cq] - M);
+        L += f * sm_ml[w][1][cq];
+        O += f * reinterpret_cast<const float*>(ring[w])[cq * D + d];
       }
     }
     const int hq = h * G + cq;
     const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
-    const float val = (L > 0.f) ? O * (1.0f / 32768.0f) / L * vs : 0.f;
+    const float val = (L > 0.f) ? O * (1.0f / kPScale) / L * vs : 0.f;
     if (S == 1) {
       reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
     } else {
@@ -333,16 +499,27 @@ bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype)
          block_size >= 16 && block_size % 16 == 0 && (q_dtype == DT_F16 || q_dtype == DT_BF16);
 }
 
-template <int D, int KVF, int SM>
-static int launch_dq(const AttnArgs& a, hipStream_t st) {
+template <int D, int KVF, int SM, int NW, int NS>
+static int launch_dqw(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.hkv, a.batch, a.num_splits);
   if (a.q_dtype == DT_F16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16>), grid, dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16, NW, NS>), grid, dim3(NW * 64), 0, st,
+                       a, a.block_table);
   else if (a.q_dtype == DT_BF16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, bf16>), grid, dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, bf16, NW, NS>), grid, dim3(NW * 64), 0,
+                       st, a, a.block_table);
   else
     return -1;
   return 0;
+}
+
+// Waves per workgroup: enough tiles per wave to amortise the set-up, and at
+// most one tile per wave per 256-key chunk of split decode.
+template <int D, int KVF, int SM>
+static int launch_dq(const AttnArgs& a, hipStream_t st) {
+  const long keys_per_wg = (long)a.max_kv_len / a.num_splits;
+  if (keys_per_wg <= 512) return launch_dqw<D, KVF, SM, 4, 2>(a, st);
+  return launch_dqw<D, KVF, SM, 12, 1>(a, st);
 }
 
 template <int D>

@@ -41,6 +41,8 @@ struct AttnArgs {
   int q_dtype, kv_format, scale_mode;
   int num_splits;       // 1 = single pass (no partials)
   int max_query_len;    // exact, from the host cum_q
+  int max_kv_len;       // longest sequence with new rows (host)
+  int block_size_log2;  // block_size is a power of two
   float softmax_scale;  // already resolved (> 0)
 };
 

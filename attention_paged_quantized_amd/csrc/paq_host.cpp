@@ -244,6 +244,8 @@ paq::AttnArgs attn_args(const paq_desc* d, const void* query, void* out, const v
   a.scale_mode = d->scale_mode;
   a.num_splits = p.num_splits > 0 ? p.num_splits : 1;
   a.max_query_len = p.max_query_len;
+  a.max_kv_len = p.max_kv_len;
+  a.block_size_log2 = __builtin_ctz((unsigned)d->block_size);
   a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d->head_size);
   return a;
 }

@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the paged quantized-KV attention path on one MI355X.
+
+One step = the whole hot path over one batch: host planning, kv_quant_append
+of the step's new tokens, then paged_attn_decode (single pass, or split-KV +
+combine) or paged_attn_prefill.  Inputs are seeded synthetic workloads
+(workloads/), resident in HBM before the timed region.  The KV cache is
+rotated over several pools (>= ~1 GiB in total) so that every step reads it
+cold from HBM rather than from the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is the decode KV-cache bandwidth (algorithmic
+KV bytes read per step / step time, GB/s) for decode workloads, or the
+algorithmic MFMA rate (TFLOP/s, unmasked causal pairs only) for prefill.
+`roofline` is measured for the dominant kernel (the attention call) with HIP
+events on its stream; `cpu_baseline` times the fp64 oracle on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-cache GB/s (frac of HBM peak) + tokens/s; prefill MFMA util"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, 256 CU x 4096 flop/clk x 2.4 GHz
+KERNEL_SOURCES = {
+    "decode": ["decode_mfma.hip", "combine.hip", "device.hpp"],
+    "prefill": ["prefill_mfma.hip", "device.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="int8_decode",
+                    choices=["int8_decode", "int4_long", "tiny_decode", "int8_prefill",
+                             "fp8_prefill"])
+    ap.add_argument("--pools", type=int, default=0, help="KV pools to rotate (0 = auto)")
+    ap.add_argument("--splits", type=int, default=None, help="override num_splits (decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kv_bytes(w):
+    act = w.q_lens > 0
+    return int((w.kv_lens[act].astype(np.int64)).sum()) * w.kv_num_heads * 2 * w.cache_head_size
+
+
+def prefill_flops(w):
+    n = w.q_lens.astype(np.int64)
+    p = w.past_lens.astype(np.int64)
+    pairs = (n * p + n * (n + 1) // 2).sum()
+    return int(4 * w.head_size * w.num_heads * pairs)
+
+
+def source_sha(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "attention_paged_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters(workload, kind, launch_bytes):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_sha") != source_sha(kind):
+        return None
+    return int((c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"]) * 1024)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    same workload: its sequences one after another (cycling through the batch)
+    until the time budget is spent; each costs one oracle quant_append of the
+    sequence's new rows plus its oracle attention."""
+    import threadpoolctl
+    from oracle import attention, quant
+    from tests.oracle_cases import f32, oracle_caches
+
+    kc, vc = oracle_caches(w)
+    kin, vin = f32(w.new_key), f32(w.new_value)
+    q = f32(w.query)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    active = [b for b in range(w.batch) if w.q_lens[b] > 0]
+    done_kv = done_flops = done_tok = nseq = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        b = active[nseq % len(active)]
+        r0, r1 = int(w.cum_q[b]), int(w.cum_q[b + 1])
+        cq = np.array([0, r1 - r0], np.int32)
+        bt = w.block_table[b:b + 1]
+        pl = w.past_lens[b:b + 1]
+        kc2, vc2 = quant.quant_append(kc, vc, kin[r0:r1], vin[r0:r1], w.k_scale, w.v_scale,
+                                      bt, cq, pl, w.kv_format)
+        attention.paged_attention(q[r0:r1], kc2, vc2, w.k_scale, w.v_scale, bt, cq, pl,
+                                  w.kv_format)
+        n, p = r1 - r0, int(w.past_lens[b])
+        done_kv += (p + n) * w.kv_num_heads * 2 * w.cache_head_size
+        done_flops += 4 * w.head_size * w.num_heads * (n * p + n * (n + 1) // 2)
+        done_tok += 1 if w.kind == "decode" else n
+        nseq += 1
+    el = time.perf_counter() - t0
+    res = {"cores": int(threads), "kind": "oracle",
+           "sample": "%d sequences of %s (cycling through the batch; fp64 oracle "
+                     "quant_append + attention per sequence), %.1f s wall" % (nseq, w.name, el),
+           "tokens_per_s": round(done_tok / el, 3)}
+    if w.kind == "decode":
+        res.update({"value": round(done_kv / el / 1e9, 5), "unit": "GB/s"})
+    else:
+        res.update({"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s"})
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_paged_quantized_amd as paq
+    import workloads
+    from tests.gpu_cases import Device, desc_for
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    paq.lib()
+    w = workloads.make(args.workload)
+    kind = w.kind
+    S = w.num_splits if args.splits is None else args.splits
+    T = w.token_count
+    print("[bench] workload %s: batch %d, tokens %d, kv bytes %.1f MB" %
+          (w.name, w.batch, T, kv_bytes(w) / 1e6), file=sys.stderr, flush=True)
+
+    pool_bytes = 2 * w.num_blocks * w.block_size * w.kv_num_heads * w.cache_head_size
+    pools = args.pools or int(min(16, max(2, -(-(1.1 * 2 ** 30) // pool_bytes))))
+    devs = [Device(w, dev).fill() for _ in range(pools)]
+    torch.cuda.synchronize()
+    print("[bench] %d KV pools of %.1f MB filled" % (pools, pool_bytes / 1e6), file=sys.stderr,
+          flush=True)
+
+    desc = desc_for(w, T)
+    kin = w.new_key.to(dev)
+    vin = w.new_value.to(dev)
+    outs = [torch.empty_like(g.query) for g in devs]
+    ws = None
+    if kind == "decode":
+        nbytes = paq.paged_attn_decode_workspace_size(desc, w.cum_q, w.past_lens, S)
+        if nbytes:
+            ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def attention(g, out):
+        if kind == "decode":
+            paq.paged_attn_decode(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                  g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0, S,
+                                  ws, stream)
+        else:
+            paq.paged_attn_prefill(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                   g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0,
+                                   stream)
+
+    def step(i, ev=None):
+        g = devs[i % pools]
+        paq.kv_quant_append(desc, w.kv_in_dtype, kin, vin, g.kc, g.vc, g.k_scale, g.v_scale,
+                            g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        attention(g, outs[i % pools])
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    kern_sorted = sorted(kern_ms)
+
+    # warm (cache-resident) reference: the same pool every call, per-call events
+    for i in range(5):
+        attention(devs[0], outs[0])
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for e0, e1 in wev:
+        e0.record(stream)
+        attention(devs[0], outs[0])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
+
+    # plain streaming copy of 1 GiB for context (read + write bytes / time)
+    src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "f16" if w.q_dtype != "bf16" else "bf16",
+              "data": "synthetic (seeded; workloads/%s)" % w.name}
+    if w.q_dtype == "f32":
+        result["dtype"] = "f32"
+    cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
+           "kv_num_heads": w.kv_num_heads, "head_size": w.head_size,
+           "block_size": w.block_size, "kv_format": w.kv_format, "scale_mode": w.scale_mode,
+           "q_dtype": w.q_dtype, "token_count": T, "kv_pools": pools}
+    if kind == "decode":
+        kvb = kv_bytes(w)
+        act = int((w.q_lens > 0).sum())
+        result.update({"value": round(kvb / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s",
+                       "tokens_per_s": round(act / (ms_step / 1e3), 1),
+                       "hbm_frac": round(kvb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
+        cfg.update({"num_splits": S, "kv_bytes_per_step": kvb,
+                    "max_kv_len": int(w.kv_lens.max())})
+        achieved = kvb / (kern_avg / 1e3) / 1e9
+        traffic = counters(w.name, "decode", kvb)
+        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                              "kernel": "paged_attn_decode call (%s)" %
+                                        ("decode_mfma" + (" + combine" if S > 1 else "")),
+                              "kernel_us_avg": round(kern_avg * 1e3, 3),
+                              "kernel_us_p10_p90": [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
+                                                    round(kern_sorted[9 * len(kern_ms) // 10] * 1e3, 3)],
+                              "warm_cache_us": round(warm_ms * 1e3, 3),
+                              "algorithmic_bytes_per_launch": kvb}
+    else:
+        fl = prefill_flops(w)
+        peak = MFMA_PEAK_TFLOPS[w.q_dtype]
+        result.update({"value": round(fl / (ms_step / 1e3) / 1e12, 3), "unit": "TFLOP/s",
+                       "tokens_per_s": round(T / (ms_step / 1e3), 1)})
+        achieved = fl / (kern_avg / 1e3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                              "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                              "traffic": counters(w.name, "prefill", fl),
+                              "kernel": "paged_attn_prefill call (prefill_mfma)",
+                              "kernel_us_avg": round(kern_avg * 1e3, 3),
+                              "warm_cache_us": round(warm_ms * 1e3, 3),
+                              "algorithmic_flops_per_launch": fl}
+        cfg.update({"max_query_len": int(w.q_lens.max()), "causal": True})
+    result["config"] = cfg
+    result["hbm_copy_GBs"] = round(copy_gbs, 1)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host (%.0f s budget)" % args.cpu_seconds,
+              file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

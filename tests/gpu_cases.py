@@ -10,7 +10,8 @@ import numpy as np
 import torch
 
 import attention_paged_quantized_amd as paq
-from tests.oracle_cases import POISON
+
+POISON = 0x7F          # same poison byte as the oracle-side pools
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
