@@ -36,7 +36,7 @@ namespace paq {
 constexpr int kDecWaves = 8;
 constexpr int kDecMaxGroup = 8;
 constexpr float kMaxSlack = 8.0f;          // lazy running-max slack (log2 units)
-constexpr float kPScale = 128.0f;          // fp16 P = p * 2^7, p <= 2^8 -> <= 2^15
+constexpr float kPScaleLog2 = 7.0f;        // fp16 P = p * 2^7, p <= 2^8 -> <= 2^15
 
 template <int KVF, int D> struct KvGeom {
   static constexpr int C = (KVF == KV_INT4) ? D / 2 : D;      // bytes per row
@@ -290,20 +290,21 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0op, qlo[m], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1op, qlo[m], s1, 0, 0, 0);
   }
-  // scale to log2 units, mask keys past the chunk
+  // mask keys past the chunk (raw scores; c2 > 0 so maxima commute with it)
   float v[8];
   float lm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v[r] = (k0 + 4 * grp + r < kend) ? s0[r] * c2 : -INFINITY;
-    v[4 + r] = (k0 + 16 + 4 * grp + r < kend) ? s1[r] * c2 : -INFINITY;
+    v[r] = (k0 + 4 * grp + r < kend) ? s0[r] : -INFINITY;
+    v[4 + r] = (k0 + 16 + 4 * grp + r < kend) ? s1[r] : -INFINITY;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) lm = fmaxf(lm, v[i]);
+  lm *= c2;
   // The reference maximum of a column is shared by its four lane rows and only
   // moves when a score exceeds it by more than kMaxSlack (log2 units): then the
   // rows exchange their maxima and the accumulators are rescaled.  Otherwise
-  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^kPScale-scaled fp16 P holds.
+  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^7-scaled fp16 P holds.
   if (__ballot(lm > st.m + kMaxSlack)) {
     const float m_new = fmaxf(st.m, rows_max(lm));
     const float alpha = fast_exp2(st.m - m_new);         // 0 on the first update
@@ -312,13 +313,15 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
 #pragma unroll
     for (int i = 0; i < NPV; ++i) st.o[i] *= alpha;
   }
+  // P' = 2^7 * 2^(s*c2 - m); the running sum carries the same factor
+  const float bias = kPScaleLog2 - st.m;
   f16x8 pop;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float p = fast_exp2(v[i] - st.m);
+    const float p = fast_exp2(fmaf(v[i], c2, bias));
     psum += p;
-    pop[i] = (f16)(p * kPScale);
+    pop[i] = (f16)p;
   }
   st.l += psum;
   // O^T += V^T P^T
@@ -483,13 +486,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
     }
     const int hq = h * G + cq;
     const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
-    const float val = (L > 0.f) ? O * (1.0f / kPScale) / L * vs : 0.f;
+    const float val = (L > 0.f) ? O / L * vs : 0.f;          // both carry 2^7
     if (S == 1) {
       reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
     } else {
       const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
       a.part_o[pi * D + d] = val;
-      if (d == 0) a.part_lse[pi] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      if (d == 0) a.part_lse[pi] = (L > 0.f) ? (M + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
     }
   }
 }

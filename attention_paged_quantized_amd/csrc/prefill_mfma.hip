@@ -15,8 +15,7 @@
 //   * all 256 threads load the codes of the next tile while the current one is
 //     computed, then convert them exactly to 16-bit values in LDS (double
 //     buffered): K row-major, V transposed (channel-major) with keys in the order
-//     the PV operand wants; 16-byte chunks are XOR-swizzled to avoid LDS bank
-//     conflicts;
+//     the PV operand wants; rows are padded by 16 bytes against bank conflicts;
 //   * S^T = K Q'^T: A = 32 keys x 16 channels of K, B = Q'^T (lane: query column
 //     l%32), so every lane owns one query column and reduces its softmax row
 //     with a single cross-lane exchange (lanes l and l^32);
@@ -38,11 +37,10 @@ namespace paq {
 
 namespace {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kBN = 64;                      // keys per KV tile
+constexpr int kPfWavesPerGroup = 8;          // waves per workgroup (32/G tokens each)
 constexpr float kPfSlack = 8.0f;             // lazy running-max slack (log2 units)
-constexpr float kPfPScale = 128.0f;          // fp16 P = p * 2^7
+constexpr float kPfPScaleLog2 = 7.0f;        // fp16 P = p * 2^7
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -60,17 +58,19 @@ template <> struct mfma32<bf16> {
   }
 };
 
-template <int KVF, int D> struct PfGeo {
+template <int KVF, int D, int NT = 256> struct PfGeo {
   static constexpr int C = (KVF == KV_INT4) ? D / 2 : D;     // bytes per cache row
   static constexpr int CPU = (KVF == KV_INT4) ? 32 : 16;     // channels per 16-byte unit
   static constexpr int UPR = C / 16;                         // 16-byte units per row
   static constexpr int KUNITS = kBN * UPR;                   // K units per tile
-  static constexpr int KU_PER_T = (KUNITS + kPfThreads - 1) / kPfThreads;   // per thread
+  static constexpr int KU_PER_T = (KUNITS + NT - 1) / NT;   // per thread
   static constexpr int VUNITS = (kBN / 2) * UPR;             // V units (key pairs)
-  static constexpr int VU_PER_T = (VUNITS + kPfThreads - 1) / kPfThreads;
-  static constexpr int KROW = D * 2;                         // bytes of a K row in LDS
-  static constexpr int KCH = D / 8;                          // 16-byte chunks per K row
-  static constexpr int VROW = kBN * 2;                       // bytes of a V^T row in LDS
+  static constexpr int VU_PER_T = (VUNITS + NT - 1) / NT;
+  // LDS rows are padded by 16 bytes: 16 lanes reading the same 16-byte column
+  // of 16 consecutive rows then hit 16 different 4-bank groups, and every
+  // address is a per-lane base plus an immediate offset
+  static constexpr int KROW = D * 2 + 16;                    // bytes of a K row in LDS
+  static constexpr int VROW = kBN * 2 + 16;                  // bytes of a V^T row in LDS
   static constexpr int TILE = kBN * KROW + D * VROW;         // one LDS buffer
 };
 
@@ -108,27 +108,27 @@ __device__ __forceinline__ void decode_unit<KV_INT4, f16>(const u32x4& w, uint32
     out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p67) - bias);
   }
 }
-// FP8 E4M3 -> fp16 (exact)
+// FP8 E4M3 -> fp16 (exact): packed OCP-E4M3 -> fp32, then fp32 -> fp16
 template <>
 __device__ __forceinline__ void decode_unit<KV_FP8, f16>(const u32x4& w, uint32_t (&out)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __builtin_bit_cast(uint32_t, e4m3_hi_bytes_to_f16x2(perm(w[i], w[i], 0x010C000Cu)));
-    out[2 * i + 1] =
-        __builtin_bit_cast(uint32_t, e4m3_hi_bytes_to_f16x2(perm(w[i], w[i], 0x030C020Cu)));
+    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
+    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
+    out[2 * i] = __builtin_bit_cast(uint32_t, (f16x2){(f16)f0[0], (f16)f0[1]});
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, (f16x2){(f16)f1[0], (f16)f1[1]});
   }
 }
-// FP8 E4M3 -> bf16 (exact, via fp32)
+// FP8 E4M3 -> bf16 (exact): gfx950's packed OCP-E4M3 -> fp32 conversion, then
+// fp32 -> bf16 (the values have 3 mantissa bits, so no rounding happens)
 template <>
 __device__ __forceinline__ void decode_unit<KV_FP8, bf16>(const u32x4& w, uint32_t (&out)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16 a = (bf16)e4m3_to_f32((w[i] >> (16 * j)) & 0xFFu);
-      const bf16 b = (bf16)e4m3_to_f32((w[i] >> (16 * j + 8)) & 0xFFu);
-      out[2 * i + j] = __builtin_bit_cast(uint32_t, (bf16x2){a, b});
-    }
+    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
+    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
+    out[2 * i] = __builtin_bit_cast(uint32_t, (bf16x2){(bf16)f0[0], (bf16)f0[1]});
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, (bf16x2){(bf16)f1[0], (bf16)f1[1]});
   }
 }
 // bf16 QK is only used with FP8 per-head scales; the other formats never ask
@@ -166,10 +166,12 @@ __device__ __forceinline__ int vt_pos(int k) {
   return 16 * c + 8 * eta + j;
 }
 
-template <int D, int KVF, int SM, typename TQ, typename TK>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
+template <int D, int KVF, int SM, typename TQ, typename TK, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
-  using Geo = PfGeo<KVF, D>;
+  constexpr int kPfThreads = NW * 64;
+  constexpr int kPfWaves = NW;
+  using Geo = PfGeo<KVF, D, NW * 64>;
   using MK = mfma32<TK>;
   typedef typename MK::vec kvec;
   constexpr int C = Geo::C;
@@ -204,16 +206,44 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][Geo::TILE];
 
   // ---- staging: codes of a tile -> registers -> converted LDS tile ----
-  u32x4 kraw[Geo::KU_PER_T], vraw[Geo::VU_PER_T][2];
-  auto load_codes = [&](int kt) {
+  // The physical blocks of a 64-key tile (at most 4 with 16-token blocks) are
+  // wave-uniform, so they are fetched with scalar loads one tile ahead.
+  const int nbt = (kBN >> lbs) > 0 ? (kBN >> lbs) : 1;       // blocks per tile (<= 4)
+  const int last_blk = (kv_end - 1) >> lbs;
+  struct TileBlocks { int32_t b[4]; };
+  auto tile_blocks = [&](int kt) {
+    TileBlocks t;
+    const int first = (kt * kBN) >> lbs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.b[j] = table[min(first + min(j, nbt - 1), last_blk)];
+    return t;
+  };
+  auto row_off = [&](const TileBlocks& tb, int kt, int k) -> size_t {
+    const int key = min(kt * kBN + k, kv_end - 1);
+    const int j = (key >> lbs) - ((kt * kBN) >> lbs);      // 0..nbt-1
+    const int32_t blk = j == 0 ? tb.b[0] : j == 1 ? tb.b[1] : j == 2 ? tb.b[2] : tb.b[3];
+    return ((size_t)blk << lbs | (key & (bs - 1))) * row_stride;
+  };
+  // raw codes of one tile, held by this thread (two sets: tiles kt+1 and kt+2
+  // are in flight while tile kt is computed)
+  // The load addresses are kept in the set and stay live until the set is
+  // stored: otherwise the compiler may hand their registers to the MFMA
+  // accumulators of the current tile and then drain the loads to avoid
+  // overwriting a vector-memory source operand.
+  struct RawSet {
+    u32x4 k[Geo::KU_PER_T];
+    u32x4 v[Geo::VU_PER_T][2];
+    const uint8_t* ka[Geo::KU_PER_T];
+    const uint8_t* va[Geo::VU_PER_T][2];
+  };
+  auto load_codes = [&](RawSet& rs, const TileBlocks& tb, int kt) {
 #pragma unroll
     for (int i = 0; i < Geo::KU_PER_T; ++i) {
       const int u = tid + i * kPfThreads;
       if (Geo::KUNITS % kPfThreads && u >= Geo::KUNITS) break;
       const int k = u / Geo::UPR, c = u % Geo::UPR;
-      const int key = min(kt * kBN + k, kv_end - 1);
-      const size_t off = ((size_t)table[key >> lbs] << lbs | (key & (bs - 1))) * row_stride;
-      kraw[i] = *reinterpret_cast<const u32x4*>(kbase + off + 16 * c);
+      rs.ka[i] = kbase + row_off(tb, kt, k) + 16 * c;
+      rs.k[i] = *reinterpret_cast<const u32x4*>(rs.ka[i]);
     }
 #pragma unroll
     for (int i = 0; i < Geo::VU_PER_T; ++i) {
@@ -222,13 +252,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       const int m = u / Geo::UPR, c = u % Geo::UPR;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int key = min(kt * kBN + 2 * m + e, kv_end - 1);
-        const size_t off = ((size_t)table[key >> lbs] << lbs | (key & (bs - 1))) * row_stride;
-        vraw[i][e] = *reinterpret_cast<const u32x4*>(vbase + off + 16 * c);
+        rs.va[i][e] = vbase + row_off(tb, kt, 2 * m + e) + 16 * c;
+        rs.v[i][e] = *reinterpret_cast<const u32x4*>(rs.va[i][e]);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto keep_addresses = [&](const RawSet& rs) {
+#pragma unroll
+    for (int i = 0; i < Geo::KU_PER_T; ++i) asm volatile("" ::"v"(rs.ka[i]));
+#pragma unroll
+    for (int i = 0; i < Geo::VU_PER_T; ++i) asm volatile("" ::"v"(rs.va[i][0]), "v"(rs.va[i][1]));
+  };
+  auto store_tile = [&](const RawSet& rs, int buf) {
+    keep_addresses(rs);
     uint8_t* kl = lds[buf];
     uint8_t* vl = lds[buf] + kBN * Geo::KROW;
 #pragma unroll
@@ -237,15 +273,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       if (Geo::KUNITS % kPfThreads && u >= Geo::KUNITS) break;
       const int k = u / Geo::UPR, c = u % Geo::UPR;
       uint32_t w[Geo::CPU / 2];
-      decode_unit<KVF, TK>(kraw[i], w);
+      decode_unit<KVF, TK>(rs.k[i], w);
       // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
 #pragma unroll
-      for (int j = 0; j < Geo::CPU / 8; ++j) {
-        const int chunk = (Geo::CPU / 8) * c + j;
-        const int phys = chunk ^ (k & (Geo::KCH - 1));
-        *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 16 * phys) =
+      for (int j = 0; j < Geo::CPU / 8; ++j)
+        *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 2 * Geo::CPU * c + 16 * j) =
             (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
-      }
     }
 #pragma unroll
     for (int i = 0; i < Geo::VU_PER_T; ++i) {
@@ -253,22 +286,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
       if (Geo::VUNITS % kPfThreads && u >= Geo::VUNITS) break;
       const int m = u / Geo::UPR, c = u % Geo::UPR;
       uint32_t w0[Geo::CPU / 2], w1[Geo::CPU / 2];
-      decode_unit<KVF, f16>(vraw[i][0], w0);
-      decode_unit<KVF, f16>(vraw[i][1], w1);
+      decode_unit<KVF, f16>(rs.v[i][0], w0);
+      decode_unit<KVF, f16>(rs.v[i][1], w1);
       const int pos = vt_pos(2 * m);                       // even: keys 2m, 2m+1 adjacent
 #pragma unroll
       for (int j = 0; j < Geo::CPU; ++j) {
         const int d = Geo::CPU * c + j;
-        const uint32_t lo = (j & 1) ? (w0[j >> 1] >> 16) : (w0[j >> 1] & 0xFFFFu);
-        const uint32_t hi = (j & 1) ? (w1[j >> 1] >> 16) : (w1[j >> 1] & 0xFFFFu);
-        const int phys = (pos >> 3) ^ (d & 7);
-        *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 16 * phys + 2 * (pos & 7)) =
-            lo | (hi << 16);
+        // {key 2m, key 2m+1} of channel d: the matching halves of w0, w1
+        const uint32_t pair = perm(w1[j >> 1], w0[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 2 * pos) = pair;
       }
     }
   };
 
-  if (ntiles > 0) load_codes(0);
+  RawSet ra, rb;
+  TileBlocks tb_next = tile_blocks(0);
+  if (ntiles > 0) load_codes(ra, tb_next, 0);
+  tb_next = tile_blocks(1);
+  if (ntiles > 1) load_codes(rb, tb_next, 1);
+  tb_next = tile_blocks(2);
 
   // ---- query operand: Q'^T columns, fold of the key scale ----
   const int my_tok = min(tok0 + wave * TPW + n / G, qlen - 1);      // clamp padded rows
@@ -305,44 +341,53 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
 
-  if (ntiles > 0) store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
+  auto compute = [&](int kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_codes(kt + 1);
     const int key0 = kt * kBN;
     if (key0 <= wave_lim) {
       const uint8_t* kl = lds[buf];
       const uint8_t* vl = lds[buf] + kBN * Geo::KROW;
-      // S^T for the two 32-key blocks
-      f32x16 s[2];
+      // S^T for the two 32-key blocks.  All K operands of a block are read
+      // before its MFMAs, and the second block's reads are issued between the
+      // first block's MFMAs, so no MFMA waits on the LDS read just before it.
+      f32x16 s[2] = {(f32x16){}, (f32x16){}};
+      {
+        const uint8_t* k0p = kl + n * Geo::KROW + 16 * eta;
+        const uint8_t* k1p = k0p + 32 * Geo::KROW;
+        kvec ka[NKK];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = (f32x16){};
-        const int k = 32 * st + n;
+        for (int kk = 0; kk < NKK; ++kk) ka[kk] = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const int phys = (2 * kk + eta) ^ (k & (Geo::KCH - 1));
-          const kvec kop = *reinterpret_cast<const kvec*>(kl + k * Geo::KROW + 16 * phys);
-          s[st] = MK::run(kop, qop[kk], s[st]);
+          s[0] = MK::run(ka[kk], qop[kk], s[0]);
+          ka[kk] = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
         }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) s[1] = MK::run(ka[kk], qop[kk], s[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NKK, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // scale, causal mask, lazy running max
+      // causal mask on raw scores, lazy running max in log2 units
       const bool diag = key0 + kBN - 1 > past + tok0 + wave * TPW;   // may need masking
       float lm = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = s[st][r] * c2;
           if (diag) {
             const int key = key0 + 32 * st + 8 * (r >> 2) + 4 * eta + (r & 3);
-            v = key <= row_lim ? v : -INFINITY;
+            s[st][r] = key <= row_lim ? s[st][r] : -INFINITY;
           }
-          s[st][r] = v;
-          lm = fmaxf(lm, v);
+          lm = fmaxf(lm, s[st][r]);
         }
+      lm *= c2;
       if (__ballot(lm > m_run + kPfSlack)) {
         const float m_new = fmaxf(m_run, fmaxf(lm, __shfl_xor(lm, 32, 64)));
         const float alpha = fast_exp2(m_run - m_new);
@@ -351,37 +396,71 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < NDT; ++i) o[i] *= alpha;
       }
-      // P (fp16, scaled) in the PV B-operand layout: chunk c = regs 8c..8c+7
+      // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
+      // regs 8c..8c+7); l accumulates the same scaled values
+      const float bias = kPfPScaleLog2 - m_run;
       f16x8 p[4];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(s[st][r] - m_run);
+          const float pv = fast_exp2(fmaf(s[st][r], c2, bias));
           l_run += pv;
-          p[2 * st + (r >> 3)][r & 7] = (f16)(pv * kPfPScale);
+          p[2 * st + (r >> 3)][r & 7] = (f16)pv;
         }
-      // O^T += V^T P^T
+      // O^T += V^T P^T, with the V^T operands of the next channel tile read
+      // while the current tile's MFMAs run
+      {
+        const uint8_t* vp = vl + n * Geo::VROW + 16 * eta;
+        f16x8 va[4];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 32 * dt + n;
+        for (int c = 0; c < 4; ++c) va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * c);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int phys = (2 * c + eta) ^ (d & 7);
-          const f16x8 vop = *reinterpret_cast<const f16x8*>(vl + d * Geo::VROW + 16 * phys);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, p[c], o[dt], 0, 0, 0);
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c], p[c], o[dt], 0, 0, 0);
+            if (dt + 1 < NDT)
+              va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * (dt + 1) * Geo::VROW + 32 * c);
+          }
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * (NDT - 1); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+  };
+  // tile kt+1's codes are in registers and tile kt+2's are loading while tile
+  // kt is computed; then tile kt+1 is converted into the other LDS buffer
+  if (ntiles > 0) store_tile(ra, 0);
+  __syncthreads();
+  int kt = 0;
+  while (true) {
+    if (kt >= ntiles) break;
+    if (kt + 2 < ntiles) { load_codes(ra, tb_next, kt + 2); tb_next = tile_blocks(kt + 3); }
+    compute(kt);
+    if (kt + 1 < ntiles) store_tile(rb, (kt + 1) & 1);
     __syncthreads();
+    ++kt;
+    if (kt >= ntiles) break;
+    if (kt + 2 < ntiles) { load_codes(rb, tb_next, kt + 2); tb_next = tile_blocks(kt + 3); }
+    compute(kt);
+    if (kt + 1 < ntiles) store_tile(ra, (kt + 1) & 1);
+    __syncthreads();
+    ++kt;
   }
 
   // ---- epilogue: normalise, value scale, store the rows of this wave ----
   l_run += __shfl_xor(l_run, 32, 64);
   const int tok = tok0 + wave * TPW + n / G;
   if (tok < qlen) {
-    const float inv = (l_run > 0.f) ? 1.f / (l_run * kPfPScale) : 0.f;
+    const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;       // both carry 2^7
     TQ* orow = reinterpret_cast<TQ*>(a.out) + ((size_t)(q0 + tok) * H + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -405,11 +484,12 @@ bool prefill_mfma_supports(int head_size, int group, int block_size, int q_dtype
 
 template <int D, int KVF, int SM, typename TQ, typename TK>
 static int launch_pf(const AttnArgs& a, hipStream_t st) {
+  constexpr int NW = kPfWavesPerGroup;
   const int G = a.num_heads / a.hkv;
-  const int TOK = kPfWaves * (32 / G);
+  const int TOK = NW * (32 / G);
   dim3 grid((a.max_query_len + TOK - 1) / TOK, a.hkv, a.batch);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK>), grid, dim3(kPfThreads), 0, st, a,
-                     a.block_table);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW>), grid, dim3(NW * 64), 0, st,
+                     a, a.block_table);
   return 0;
 }
 
