@@ -2,67 +2,103 @@
 // "GQA GEMV decode", section 2): for every (row, head), with chunk partials
 // (o_c, lse_c), L = log sum_c exp(lse_c) and out = sum_c exp(lse_c - L) o_c.
 // Empty chunks carry lse = -inf and contribute nothing.
+//
+// One workgroup of 4 waves per (row, head): the waves take every 4th chunk,
+// each lane owns D/64 consecutive channels (one vector load per chunk), and
+// the four partial sums meet in LDS.  The loads of a wave are independent, so
+// many are in flight at once.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace paq {
 
-constexpr int kCombineThreads = 128;
+constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = kCombineWaves * 64;
+constexpr int kCombineMaxSplits = 4096;
 
-// One workgroup per (row, head); thread t owns channels t, t+128, ...
-template <typename TO>
+template <typename TO, int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, TO* __restrict__ out,
-    const int32_t* __restrict__ cum_q, int batch, int num_heads, int head_size, int S) {
+    int num_heads, int S) {
+  constexpr int PER_LANE = D / 64;                 // 2 for D=128, 1 for D=64
   const int r = blockIdx.x / num_heads;
   const int h = blockIdx.x % num_heads;
   const size_t base = ((size_t)r * num_heads + h) * S;
-  __shared__ float w[4096];
-  __shared__ float red[kCombineThreads / 64];
-  // maximum lse
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float red[kCombineWaves];
+  __shared__ float acc_sh[kCombineWaves][D];
+  // global maximum of the chunk log-sum-exps
   float mx = -INFINITY;
-  for (int c = threadIdx.x; c < S; c += kCombineThreads) mx = fmaxf(mx, part_lse[base + c]);
+  for (int c = tid; c < S; c += kCombineThreads) mx = fmaxf(mx, part_lse[base + c]);
   mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
   mx = red[0];
-  for (int i = 1; i < kCombineThreads / 64; ++i) mx = fmaxf(mx, red[i]);
-  __syncthreads();
-  float sum = 0.f;
-  for (int c = threadIdx.x; c < S; c += kCombineThreads) {
-    const float l = part_lse[base + c];
-    const float e = (l == -INFINITY) ? 0.f : expf(l - mx);
-    w[c] = e;
-    sum += e;
+#pragma unroll
+  for (int i = 1; i < kCombineWaves; ++i) mx = fmaxf(mx, red[i]);
+  // weighted sum of the partial outputs; weights sum to 1 after division
+  float acc[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll 4
+    for (int c = wave; c < S; c += kCombineWaves) {
+      const float l = part_lse[base + c];
+      const float w = (l == -INFINITY) ? 0.f : __expf(l - mx);
+      wsum += w;
+      const float* po = part_o + (base + c) * D + PER_LANE * lane;
+      if constexpr (PER_LANE == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(po);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[1] = fmaf(w, v.y, acc[1]);
+      } else {
+        acc[0] = fmaf(w, po[0], acc[0]);
+      }
+    }
   }
-  sum = wave_sum(sum);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
+  __syncthreads();                                  // red[] reads done
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) acc_sh[wave][PER_LANE * lane + i] = acc[i];
+  if (lane == 0) red[wave] = wsum;
   __syncthreads();
-  sum = 0.f;
-  for (int i = 0; i < kCombineThreads / 64; ++i) sum += red[i];
-  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  for (int d = threadIdx.x; d < head_size; d += kCombineThreads) {
-    float acc = 0.f;
-    for (int c = 0; c < S; ++c) acc = fmaf(w[c], part_o[(base + c) * head_size + d], acc);
-    out[((size_t)r * num_heads + h) * head_size + d] = from_f32<TO>(acc * inv);
+  if (wave == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) tot += red[i];
+    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int d = PER_LANE * lane + i;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kCombineWaves; ++w) v += acc_sh[w][d];
+      out[((size_t)r * num_heads + h) * D + d] = from_f32<TO>(v * inv);
+    }
   }
 }
 
-int launch_combine(const AttnArgs& a, hipStream_t st) {
-  if (a.num_splits > 4096 || a.token_count == 0) return -1;
+template <int D>
+static int launch_combine_d(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.token_count * a.num_heads);
   switch (a.q_dtype) {
-#define PAQ_COMBINE_CASE(DTV, TYPE)                                                         \
-  case DTV:                                                                               \
-    hipLaunchKernelGGL((combine_kernel<TYPE>), grid, dim3(kCombineThreads), 0, st, a.part_o, \
-                       a.part_lse, (TYPE*)a.out, a.cum_q, a.batch, a.num_heads,             \
-                       a.head_size, a.num_splits);                                         \
+#define PAQ_COMBINE_CASE(DTV, TYPE)                                                           \
+  case DTV:                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<TYPE, D>), grid, dim3(kCombineThreads), 0, st, a.part_o, \
+                       a.part_lse, (TYPE*)a.out, a.num_heads, a.num_splits);                  \
     return 0;
     PAQ_COMBINE_CASE(DT_F32, float)
     PAQ_COMBINE_CASE(DT_F16, f16)
     PAQ_COMBINE_CASE(DT_BF16, bf16)
 #undef PAQ_COMBINE_CASE
   }
+  return -1;
+}
+
+int launch_combine(const AttnArgs& a, hipStream_t st) {
+  if (a.num_splits > kCombineMaxSplits || a.token_count == 0) return -1;
+  if (a.head_size == 128) return launch_combine_d<128>(a, st);
+  if (a.head_size == 64) return launch_combine_d<64>(a, st);
   return -1;
 }
 

@@ -33,7 +33,6 @@
 
 namespace paq {
 
-constexpr int kDecWaves = 8;
 constexpr int kDecMaxGroup = 8;
 constexpr float kMaxSlack = 8.0f;          // lazy running-max slack (log2 units)
 constexpr float kPScaleLog2 = 7.0f;        // fp16 P = p * 2^7, p <= 2^8 -> <= 2^15
@@ -332,46 +331,15 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
     st.o[nbk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[nbk], pop, st.o[nbk], 0, 0, 0);
 }
 
-template <int D, int KVF, int SM, typename TQ, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
-                                                             const int32_t* __restrict__ block_table) {
-  using Geo = KvGeom<KVF, D>;
-  using R = Ring<KVF, D>;
-  constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
-  const int h = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z;
-  const int q0 = a.cum_q[b];
-  if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
-  const int kv_len = a.past_lens[b] + 1;
-  const int bs = a.block_size, hkv = a.hkv, H = a.num_heads;
-  const int G = H / hkv;
-  const int nb = (kv_len + bs - 1) / bs;
-  const int S = a.num_splits;
-  const int kbeg = (int)(((long)chunk * nb) / S) * bs;
-  const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
-  const int lbs = a.block_size_log2;
-  const uint32_t row_stride = (uint32_t)(hkv * C);         // bytes between tokens
-  const uint8_t* kbase = a.key_cache + (size_t)h * C;
-  const uint8_t* vbase = a.value_cache + (size_t)h * C;
-  constexpr int stride = 32 * NW;
-
-  constexpr int WAVE_BYTES = NS * R::SLOT;                 // NS slots per wave
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][WAVE_BYTES];
-  uint8_t* myring = ring[wave];
-
-  // start streaming this wave's first NS tiles before the set-up work
-  const int k_first = kbeg + 32 * wave;
-  if (kbeg < kend) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      issue_tile<KVF, D>(myring + j * R::SLOT, k_first + j * stride, kend, lbs,
-                         tile_offsets(k_first + j * stride, kend, lbs, table, row_stride), kbase,
-                         vbase, row_stride, lane);
-  }
-
+// Fold the key scale into the query: Q' = Q * s / M_h with M_h the power of
+// two >= max|s| of kv head h, split into fp16 hi + lo parts in the QK B-operand
+// layout (lane col+16*grp: query column col, channels of segment grp).
+template <int D, int KVF, int SM, typename TQ>
+__device__ __forceinline__ void fold_query(const AttnArgs& a, int h, int q0, int G, int col,
+                                           int grp, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[D / 32],
+                                           float& Mh) {
+  constexpr int NQK = D / 32;
+  const int H = a.num_heads;
   // ---- fold the key scale into the query: Q' = Q * s / M, split hi + lo ----
   // lane (col, grp) holds query column col, channels [(D/4)*grp, (D/4)*(grp+1))
   constexpr int SEG = D / 4;
@@ -395,9 +363,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
   }
   int ex;
   const float fr = frexpf(smax, &ex);                      // smax = fr * 2^ex, fr in [0.5,1)
-  const float Mh = (smax == 0.f) ? 1.f : ldexpf(1.f, fr == 0.5f ? ex - 1 : ex);
+  Mh = (smax == 0.f) ? 1.f : ldexpf(1.f, fr == 0.5f ? ex - 1 : ex);
   const float invM = 1.f / Mh;                             // exact (power of two)
-  f16x8 qhi[NQK], qlo[NQK];
   {
     float qv[SEG];
 #pragma unroll
@@ -425,6 +392,56 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
       }
     }
   }
+}
+
+template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HP>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
+                                                             const int32_t* __restrict__ block_table) {
+  using Geo = KvGeom<KVF, D>;
+  using R = Ring<KVF, D>;
+  constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
+  // HP kv heads per workgroup (2 when a head's cache row is shorter than a
+  // 128-byte line: both heads' halves of every line are then read by the
+  // same CU); NW / HP waves per head
+  constexpr int NWH = NW / HP;
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x * HP + wave_all / NWH, b = blockIdx.y, chunk = blockIdx.z;
+  const int q0 = a.cum_q[b];
+  if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
+  const int kv_len = a.past_lens[b] + 1;
+  const int bs = a.block_size, hkv = a.hkv, H = a.num_heads;
+  const int G = H / hkv;
+  const int nb = (kv_len + bs - 1) / bs;
+  const int S = a.num_splits;
+  const int kbeg = (int)(((long)chunk * nb) / S) * bs;
+  const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_all % NWH;                          // wave index within its head
+  const int col = lane & 15, grp = lane >> 4;
+  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+  const int lbs = a.block_size_log2;
+  const uint32_t row_stride = (uint32_t)(hkv * C);         // bytes between tokens
+  const uint8_t* kbase = a.key_cache + (size_t)h * C;
+  const uint8_t* vbase = a.value_cache + (size_t)h * C;
+  constexpr int stride = 32 * NWH;
+
+  constexpr int WAVE_BYTES = NS * R::SLOT;                 // NS slots per wave
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][WAVE_BYTES];
+  uint8_t* myring = ring[wave_all];
+
+  // start streaming this wave's first NS tiles before the set-up work
+  const int k_first = kbeg + 32 * wave;
+  if (kbeg < kend) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      issue_tile<KVF, D>(myring + j * R::SLOT, k_first + j * stride, kend, lbs,
+                         tile_offsets(k_first + j * stride, kend, lbs, table, row_stride), kbase,
+                         vbase, row_stride, lane);
+  }
+
+  f16x8 qhi[NQK], qlo[NQK];
+  float Mh;
+  fold_query<D, KVF, SM, TQ>(a, h, q0, G, col, grp, qhi, qlo, Mh);
   const float c2 = a.softmax_scale * Mh * kLog2e;          // score -> log2 units
 
   // ---- per-wave online softmax over this wave's tiles ----
@@ -457,35 +474,37 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
   wait_vmcnt_le(0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- merge the waves through LDS (each wave writes into its own ring) ----
+  // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
   const float l_run = rows_sum(st.l);
   __shared__ float sm_ml[NW][2][kDecMaxGroup];             // running max, sum per wave
   float* wo = reinterpret_cast<float*>(myring);             // [kDecMaxGroup][D] per wave
   static_assert(kDecMaxGroup * D * 4 <= WAVE_BYTES, "merge area");
   if (col < G) {
-    if (grp == 0) { sm_ml[wave][0][col] = st.m; sm_ml[wave][1][col] = l_run; }
+    if (grp == 0) { sm_ml[wave_all][0][col] = st.m; sm_ml[wave_all][1][col] = l_run; }
 #pragma unroll
     for (int nbk = 0; nbk < NPV; ++nbk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) wo[col * D + (D / 16) * (4 * grp + r) + nbk] = st.o[nbk][r];
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += NW * 64) {
-    const int cq = t / D, d = t % D;
+  for (int t = threadIdx.x; t < HP * G * D; t += NW * 64) {
+    const int hs = t / (G * D), cq = (t / D) % G, d = t % D;
+    const int w0 = hs * NWH;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][0][cq]);
+    for (int w = 0; w < NWH; ++w) M = fmaxf(M, sm_ml[w0 + w][0][cq]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2(sm_ml[w][0][cq] - M);
-        L += f * sm_ml[w][1][cq];
-        O += f * reinterpret_cast<const float*>(ring[w])[cq * D + d];
+      for (int w = 0; w < NWH; ++w) {
+        const float f = fast_exp2(sm_ml[w0 + w][0][cq] - M);
+        L += f * sm_ml[w0 + w][1][cq];
+        O += f * reinterpret_cast<const float*>(ring[w0 + w])[cq * D + d];
       }
     }
-    const int hq = h * G + cq;
-    const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
+    const int ho = blockIdx.x * HP + hs;
+    const int hq = ho * G + cq;
+    const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
     const float val = (L > 0.f) ? O / L * vs : 0.f;          // both carry 2^7
     if (S == 1) {
       reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
@@ -497,19 +516,114 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-KV decode: one wave per (kv head, chunk).  A workgroup holds the (up
+// to) 8 kv heads of one (sequence, chunk), so every token row of the chunk is
+// read by one CU, and each wave streams its chunk through its own LDS ring with
+// no cross-wave merge or barrier.  Each wave writes the normalised partial
+// output and log-sum-exp of its G query heads for the combine kernel.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+
+template <int D, int KVF, int SM, typename TQ, int NS>
+__global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(
+    AttnArgs a, const int32_t* __restrict__ block_table) {
+  using Geo = KvGeom<KVF, D>;
+  using R = Ring<KVF, D>;
+  constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x * kSplitWaves + wave, b = blockIdx.y, chunk = blockIdx.z;
+  if (h >= a.hkv) return;                                   // no barriers below
+  const int q0 = a.cum_q[b];
+  if (a.cum_q[b + 1] == q0) return;                         // no new token: no rows
+  const int kv_len = a.past_lens[b] + 1;
+  const int bs = a.block_size, hkv = a.hkv, H = a.num_heads;
+  const int G = H / hkv;
+  const int nb = (kv_len + bs - 1) / bs;
+  const int S = a.num_splits;
+  const int kbeg = (int)(((long)chunk * nb) / S) * bs;
+  const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+  const int lbs = a.block_size_log2;
+  const uint32_t row_stride = (uint32_t)(hkv * C);
+  const uint8_t* kbase = a.key_cache + (size_t)h * C;
+  const uint8_t* vbase = a.value_cache + (size_t)h * C;
+
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSplitWaves][NS * R::SLOT];
+  uint8_t* myring = ring[wave];
+  if (kbeg < kend) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      issue_tile<KVF, D>(myring + j * R::SLOT, kbeg + 32 * j, kend, lbs,
+                         tile_offsets(kbeg + 32 * j, kend, lbs, table, row_stride), kbase, vbase,
+                         row_stride, lane);
+  }
+  f16x8 qhi[NQK], qlo[NQK];
+  float Mh;
+  fold_query<D, KVF, SM, TQ>(a, h, q0, G, col, grp, qhi, qlo, Mh);
+  const float c2 = a.softmax_scale * Mh * kLog2e;
+
+  WaveState<D> st;
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (kbeg < kend) {
+    int cur = 0;
+    TileOffsets nxt = tile_offsets(kbeg + 32 * NS, kend, lbs, table, row_stride);
+    for (int k = kbeg; k < kend; k += 32) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_le((NS - 1) * 2 * R::NI);
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* slot = myring + cur * R::SLOT;
+      TileRaw<KVF, D> t;
+      read_tile<KVF, D>(slot, t, col, grp);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      issue_tile<KVF, D>(slot, k + 32 * NS, kend, lbs, nxt, kbase, vbase, row_stride, lane);
+      nxt = tile_offsets(k + 32 * (NS + 1), kend, lbs, table, row_stride);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<KVF, D>(t, k, kend, c2, qhi, qlo, st, grp);
+      cur = (cur + 1 == NS) ? 0 : cur + 1;
+    }
+  }
+  wait_vmcnt_le(0);
+
+  // normalised partial output and log-sum-exp of this wave's G query heads
+  const float L = rows_sum(st.l);
+  if (col < G) {
+    const int hq = h * G + col;
+    const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;            // both carry 2^7
+    float* po = a.part_o + pi * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d0 = (D / 16) * (4 * grp + r);
+#pragma unroll
+      for (int nbk = 0; nbk < NPV; ++nbk) {
+        const int d = d0 + nbk;
+        const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
+        po[d] = st.o[nbk][r] * inv * vs;
+      }
+    }
+    if (grp == 0)
+      a.part_lse[pi] = (L > 0.f) ? (st.m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
+  }
+}
+
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype) {
   return (head_size == 64 || head_size == 128) && group >= 1 && group <= kDecMaxGroup &&
          block_size >= 16 && block_size % 16 == 0 && (q_dtype == DT_F16 || q_dtype == DT_BF16);
 }
 
-template <int D, int KVF, int SM, int NW, int NS>
+template <int D, int KVF, int SM, int NW, int NS, int HP>
 static int launch_dqw(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.hkv, a.batch, a.num_splits);
+  dim3 grid(a.hkv / HP, a.batch, a.num_splits);
   if (a.q_dtype == DT_F16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16, NW, NS>), grid, dim3(NW * 64), 0, st,
-                       a, a.block_table);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16, NW, NS, HP>), grid, dim3(NW * 64), 0,
+                       st, a, a.block_table);
   else if (a.q_dtype == DT_BF16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, bf16, NW, NS>), grid, dim3(NW * 64), 0,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, bf16, NW, NS, HP>), grid, dim3(NW * 64), 0,
                        st, a, a.block_table);
   else
     return -1;
@@ -517,12 +631,36 @@ static int launch_dqw(const AttnArgs& a, hipStream_t st) {
 }
 
 // Waves per workgroup: enough tiles per wave to amortise the set-up, and at
-// most one tile per wave per 256-key chunk of split decode.
+// most one tile per wave per 256-key chunk of split decode.  Rows shorter than
+// a 128-byte line (packed INT4 with D=128, any format with D=64) pair two kv
+// heads per workgroup when the head count allows.
+template <int D, int KVF, int SM>
+static int launch_split(const AttnArgs& a, hipStream_t st) {
+  dim3 grid((a.hkv + kSplitWaves - 1) / kSplitWaves, a.batch, a.num_splits);
+  if (a.q_dtype == DT_F16)
+    hipLaunchKernelGGL((decode_split_kernel<D, KVF, SM, f16, 2>), grid, dim3(kSplitWaves * 64), 0,
+                       st, a, a.block_table);
+  else if (a.q_dtype == DT_BF16)
+    hipLaunchKernelGGL((decode_split_kernel<D, KVF, SM, bf16, 2>), grid, dim3(kSplitWaves * 64),
+                       0, st, a, a.block_table);
+  else
+    return -1;
+  return 0;
+}
+
+// Single pass: one workgroup per (sequence, kv head) whose waves take the
+// tiles in turn and merge at the end; rows shorter than a 128-byte line
+// (packed INT4 with D=128, any format with D=64) pair two kv heads per
+// workgroup so both halves of every line are read by the same CU.  Split-KV:
+// one wave per (kv head, chunk).
 template <int D, int KVF, int SM>
 static int launch_dq(const AttnArgs& a, hipStream_t st) {
-  const long keys_per_wg = (long)a.max_kv_len / a.num_splits;
-  if (keys_per_wg <= 512) return launch_dqw<D, KVF, SM, 4, 2>(a, st);
-  return launch_dqw<D, KVF, SM, 12, 1>(a, st);
+  if (a.num_splits > 1) return launch_split<D, KVF, SM>(a, st);
+  constexpr bool short_rows = KvGeom<KVF, D>::C < 128;
+  if constexpr (short_rows) {
+    if (a.hkv % 2 == 0) return launch_dqw<D, KVF, SM, 12, 2, 2>(a, st);
+  }
+  return launch_dqw<D, KVF, SM, 12, 1, 1>(a, st);
 }
 
 template <int D>
