@@ -198,11 +198,12 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     if (hh >= G) break;
     const int h = g * G + hh;
     const float l = l_sh[hh];
-    const float o = (l > 0.f) ? acc[hh] * vs / l : 0.f;
+    const float o = (l > 0.f) ? acc[hh] / l : 0.f;
     if (S == 1) {
       TQ* out = reinterpret_cast<TQ*>(a.out);
-      out[((size_t)r * H + h) * D + my_d] = from_f32<TQ>(o);
+      out[((size_t)r * H + h) * D + my_d] = from_f32<TQ>(o * vs);
     } else {
+      // split-KV partials leave the value scale to the combine
       const size_t pi = ((size_t)r * H + h) * S + chunk;
       a.part_o[pi * D + my_d] = o;
       if (my_d == 0) a.part_lse[pi] = (l > 0.f) ? m_sh[hh] + logf(l) : -INFINITY;

@@ -1,7 +1,9 @@
 // combine.hip -- log-sum-exp merge of split-KV partials (flash decoding,
 // "GQA GEMV decode", section 2): for every (row, head), with chunk partials
 // (o_c, lse_c), L = log sum_c exp(lse_c) and out = sum_c exp(lse_c - L) o_c.
-// Empty chunks carry lse = -inf and contribute nothing.
+// Empty chunks carry lse = -inf and contribute nothing.  The partial outputs
+// are sums of probability-weighted value codes; the per-channel (or per-head)
+// value scale, the same for every chunk, is applied here once.
 //
 // One workgroup of 4 waves per (row, head): the waves take every 4th chunk,
 // each lane owns D/64 consecutive channels (one vector load per chunk), and
@@ -19,7 +21,7 @@ constexpr int kCombineMaxSplits = 4096;
 template <typename TO, int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, TO* __restrict__ out,
-    int num_heads, int S) {
+    const float* __restrict__ v_scale, int num_heads, int group, int per_channel, int S) {
   constexpr int PER_LANE = D / 64;                 // 2 for D=128, 1 for D=64
   const int r = blockIdx.x / num_heads;
   const int h = blockIdx.x % num_heads;
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (lane == 0) red[wave] = wsum;
   __syncthreads();
   if (wave == 0) {
+    const int hk = h / group;                                 // kv head of query head h
     float tot = 0.f;
 #pragma unroll
     for (int i = 0; i < kCombineWaves; ++i) tot += red[i];
@@ -73,7 +76,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kCombineWaves; ++w) v += acc_sh[w][d];
-      out[((size_t)r * num_heads + h) * D + d] = from_f32<TO>(v * inv);
+      const float vs = per_channel ? v_scale[hk * D + d] : v_scale[hk];
+      out[((size_t)r * num_heads + h) * D + d] = from_f32<TO>(v * inv * vs);
     }
   }
 }
@@ -85,7 +89,8 @@ static int launch_combine_d(const AttnArgs& a, hipStream_t st) {
 #define PAQ_COMBINE_CASE(DTV, TYPE)                                                           \
   case DTV:                                                                                 \
     hipLaunchKernelGGL((combine_kernel<TYPE, D>), grid, dim3(kCombineThreads), 0, st, a.part_o, \
-                       a.part_lse, (TYPE*)a.out, a.num_heads, a.num_splits);                  \
+                       a.part_lse, (TYPE*)a.out, a.v_scale, a.num_heads, a.num_heads / a.hkv,   \
+                       a.scale_mode == SCALE_CHANNEL ? 1 : 0, a.num_splits);                  \
     return 0;
     PAQ_COMBINE_CASE(DT_F32, float)
     PAQ_COMBINE_CASE(DT_F16, f16)

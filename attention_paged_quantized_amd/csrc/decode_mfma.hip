@@ -67,10 +67,9 @@ __device__ __forceinline__ f16x8 k_operand(const uint32_t* kw, int m) {
     f16x2 c = i8pair_to_f16x2(w1, 0x04010400u), d = i8pair_to_f16x2(w1, 0x04030402u);
     r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   } else if constexpr (KVF == KV_INT4) {
-    const uint32_t w = kw[m] ^ 0x88888888u;
-    f16x2 a = nib_to_f16x2(w, 0), b = nib_to_f16x2(w, 4);
-    f16x2 c = nib_to_f16x2(w, 8), d = nib_to_f16x2(w, 12);
-    r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    f16x2 p[4];
+    int4x8_to_f16x2x4(kw[m], p);
+    r = (f16x8){p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
   } else {
     const uint32_t w0 = kw[2 * m], w1 = kw[2 * m + 1];
     f16x2 a = e4m3_hi_bytes_to_f16x2(perm(w0, w0, 0x010C000Cu));
@@ -120,13 +119,13 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vw)[8][2], f16x8 (&v
         // bytes [e.bj, e.bj+1, e+1.bj, e+1.bj+1]
         const uint32_t sel = (uint32_t)j | ((uint32_t)(j + 1) << 8) | ((uint32_t)(4 + j) << 16) |
                              ((uint32_t)(5 + j) << 24);
-        const uint32_t x = perm(vw[e + 1][0], vw[e][0], sel) ^ 0x88888888u;
-        const f16x2 c0 = nib_to_f16x2(x, 0), c1 = nib_to_f16x2(x, 4);
-        const f16x2 c2 = nib_to_f16x2(x, 8), c3 = nib_to_f16x2(x, 12);
-        vop[2 * j][e] = c0[0]; vop[2 * j][e + 1] = c0[1];
-        vop[2 * j + 1][e] = c1[0]; vop[2 * j + 1][e + 1] = c1[1];
-        vop[2 * j + 2][e] = c2[0]; vop[2 * j + 2][e + 1] = c2[1];
-        vop[2 * j + 3][e] = c3[0]; vop[2 * j + 3][e + 1] = c3[1];
+        f16x2 c[4];
+        int4x8_to_f16x2x4(perm(vw[e + 1][0], vw[e][0], sel), c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vop[2 * j + i][e] = c[i][0];
+          vop[2 * j + i][e + 1] = c[i][1];
+        }
       }
     }
   }
@@ -151,17 +150,12 @@ template <int KVF, int D> struct Ring {
   static constexpr int SLOT = 64 * C;           // K rows + V rows
 };
 
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
   // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
   // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Queue the copy of the tile starting at key k0 into `slot` (wave-uniform).
@@ -294,8 +288,15 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
   float lm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v[r] = (k0 + 4 * grp + r < kend) ? s0[r] : -INFINITY;
-    v[4 + r] = (k0 + 16 + 4 * grp + r < kend) ? s1[r] : -INFINITY;
+    v[r] = s0[r];
+    v[4 + r] = s1[r];
+  }
+  if (k0 + 32 > kend) {                                    // tile cut by the end (uniform)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (k0 + 4 * grp + r >= kend) v[r] = -INFINITY;
+      if (k0 + 16 + 4 * grp + r >= kend) v[4 + r] = -INFINITY;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) lm = fmaxf(lm, v[i]);
@@ -331,67 +332,94 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
     st.o[nbk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[nbk], pop, st.o[nbk], 0, 0, 0);
 }
 
+// The raw inputs of the query fold for one lane (col, grp): query column col,
+// channels [(D/4)*grp, (D/4)*(grp+1)), as loaded from memory.  Loading them is
+// kept apart from the arithmetic so that the loads can be issued before the
+// first tile copies (vector-memory results return in order).
+template <int D, int SM> struct QueryRaw {
+  static constexpr int SEG = D / 4;
+  u32x4 q[SEG / 8];                                  // SEG 16-bit query values
+  f32x4 s[SM == SCALE_CHANNEL ? SEG / 4 : 1];         // key scales (or the head's one)
+};
+
+template <int D, int SM, typename TQ>
+__device__ __forceinline__ void load_query(const AttnArgs& a, int h, int q0, int G, int col,
+                                           int grp, QueryRaw<D, SM>& r) {
+  constexpr int SEG = D / 4;
+  if constexpr (SM == SCALE_CHANNEL) {
+    const f32x4* sp = reinterpret_cast<const f32x4*>(a.k_scale + h * D + SEG * grp);
+#pragma unroll
+    for (int i = 0; i < SEG / 4; ++i) r.s[i] = sp[i];
+  } else {
+    const float x = a.k_scale[h];
+    r.s[0] = (f32x4){x, x, x, x};
+  }
+#pragma unroll
+  for (int i = 0; i < SEG / 8; ++i) r.q[i] = (u32x4){0u, 0u, 0u, 0u};
+  if (col < G) {
+    const TQ* q = reinterpret_cast<const TQ*>(a.query) +
+                  ((size_t)q0 * a.num_heads + h * G + col) * D + SEG * grp;
+#pragma unroll
+    for (int i = 0; i < SEG / 8; ++i) r.q[i] = reinterpret_cast<const u32x4*>(q)[i];
+  }
+}
+
 // Fold the key scale into the query: Q' = Q * s / M_h with M_h the power of
 // two >= max|s| of kv head h, split into fp16 hi + lo parts in the QK B-operand
 // layout (lane col+16*grp: query column col, channels of segment grp).
 template <int D, int KVF, int SM, typename TQ>
-__device__ __forceinline__ void fold_query(const AttnArgs& a, int h, int q0, int G, int col,
-                                           int grp, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[D / 32],
-                                           float& Mh) {
+__device__ __forceinline__ void fold_loaded_query(const QueryRaw<D, SM>& r, f16x8 (&qhi)[D / 32],
+                                                  f16x8 (&qlo)[D / 32], float& Mh) {
   constexpr int NQK = D / 32;
-  const int H = a.num_heads;
-  // ---- fold the key scale into the query: Q' = Q * s / M, split hi + lo ----
-  // lane (col, grp) holds query column col, channels [(D/4)*grp, (D/4)*(grp+1))
   constexpr int SEG = D / 4;
   float sv[SEG];
   float smax;
   if constexpr (SM == SCALE_CHANNEL) {
-    const f32x4* sp = reinterpret_cast<const f32x4*>(a.k_scale + h * D + SEG * grp);
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
-      const f32x4 x = sp[i];
-      sv[4 * i] = x[0]; sv[4 * i + 1] = x[1]; sv[4 * i + 2] = x[2]; sv[4 * i + 3] = x[3];
+      sv[4 * i] = r.s[i][0]; sv[4 * i + 1] = r.s[i][1];
+      sv[4 * i + 2] = r.s[i][2]; sv[4 * i + 3] = r.s[i][3];
     }
     smax = 0.f;
 #pragma unroll
     for (int i = 0; i < SEG; ++i) smax = fmaxf(smax, fabsf(sv[i]));
     smax = rows_max(smax);
   } else {
-    smax = fabsf(a.k_scale[h]);
+    smax = fabsf(r.s[0][0]);
 #pragma unroll
-    for (int i = 0; i < SEG; ++i) sv[i] = a.k_scale[h];
+    for (int i = 0; i < SEG; ++i) sv[i] = r.s[0][0];
   }
   int ex;
   const float fr = frexpf(smax, &ex);                      // smax = fr * 2^ex, fr in [0.5,1)
   Mh = (smax == 0.f) ? 1.f : ldexpf(1.f, fr == 0.5f ? ex - 1 : ex);
   const float invM = 1.f / Mh;                             // exact (power of two)
-  {
-    float qv[SEG];
+  float qv[SEG];
 #pragma unroll
-    for (int i = 0; i < SEG; ++i) qv[i] = 0.f;
-    if (col < G) {
-      const TQ* q = reinterpret_cast<const TQ*>(a.query) + ((size_t)q0 * H + h * G + col) * D +
-                    SEG * grp;
+  for (int i = 0; i < SEG / 8; ++i) {
+    const TQ* e = reinterpret_cast<const TQ*>(&r.q[i]);
 #pragma unroll
-      for (int i = 0; i < SEG / 8; ++i) {
-        const u32x4 x = reinterpret_cast<const u32x4*>(q)[i];
-        const TQ* e = reinterpret_cast<const TQ*>(&x);
+    for (int j = 0; j < 8; ++j) qv[8 * i + j] = to_f32(e[j]);
+  }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qv[8 * i + j] = to_f32(e[j]);
-      }
-    }
+  for (int m = 0; m < NQK; ++m) {
 #pragma unroll
-    for (int m = 0; m < NQK; ++m) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = qk_channel<KVF, D>(0, m, e);        // channel within the segment
-        const float x = qv[c] * (sv[c] * invM);
-        const f16 hi = (f16)x;
-        qhi[m][e] = hi;
-        qlo[m][e] = (f16)(x - (float)hi);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int c = qk_channel<KVF, D>(0, m, e);          // channel within the segment
+      const float x = qv[c] * (sv[c] * invM);
+      const f16 hi = (f16)x;
+      qhi[m][e] = hi;
+      qlo[m][e] = (f16)(x - (float)hi);
     }
   }
+}
+
+template <int D, int KVF, int SM, typename TQ>
+__device__ __forceinline__ void fold_query(const AttnArgs& a, int h, int q0, int G, int col,
+                                           int grp, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[D / 32],
+                                           float& Mh) {
+  QueryRaw<D, SM> r;
+  load_query<D, SM, TQ>(a, h, q0, G, col, grp, r);
+  fold_loaded_query<D, KVF, SM, TQ>(r, qhi, qlo, Mh);
 }
 
 template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HP>
@@ -405,16 +433,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
   // same CU); NW / HP waves per head
   constexpr int NWH = NW / HP;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x * HP + wave_all / NWH, b = blockIdx.y, chunk = blockIdx.z;
+  const int h = blockIdx.x * HP + wave_all / NWH, b = blockIdx.y;
   const int q0 = a.cum_q[b];
   if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
   const int kv_len = a.past_lens[b] + 1;
-  const int bs = a.block_size, hkv = a.hkv, H = a.num_heads;
+  const int hkv = a.hkv, H = a.num_heads;
   const int G = H / hkv;
-  const int nb = (kv_len + bs - 1) / bs;
-  const int S = a.num_splits;
-  const int kbeg = (int)(((long)chunk * nb) / S) * bs;
-  const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
+  const int kbeg = 0, kend = kv_len;
   const int lane = threadIdx.x & 63;
   const int wave = wave_all % NWH;                          // wave index within its head
   const int col = lane & 15, grp = lane >> 4;
@@ -455,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
     for (int k = k_first; k < kend; k += stride) {
       // this tile's copies are done once at most the later tiles' remain
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt_le((NS - 1) * 2 * R::NI);
+      wait_vmcnt_le<(NS - 1) * 2 * R::NI>();
       __builtin_amdgcn_sched_barrier(0);
       uint8_t* slot = myring + cur * R::SLOT;
       TileRaw<KVF, D> t;
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
     }
   }
   // drain this wave's outstanding copies before its ring is reused below
-  wait_vmcnt_le(0);
+  wait_vmcnt_le<0>();
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
@@ -506,34 +531,150 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
     const int hq = ho * G + cq;
     const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
     const float val = (L > 0.f) ? O / L * vs : 0.f;          // both carry 2^7
-    if (S == 1) {
-      reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
-    } else {
-      const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
-      a.part_o[pi * D + d] = val;
-      if (d == 0) a.part_lse[pi] = (L > 0.f) ? (M + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
-    }
+    reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV decode: one wave per (kv head, chunk).  A workgroup holds the (up
-// to) 8 kv heads of one (sequence, chunk), so every token row of the chunk is
-// read by one CU, and each wave streams its chunk through its own LDS ring with
-// no cross-wave merge or barrier.  Each wave writes the normalised partial
-// output and log-sum-exp of its G query heads for the combine kernel.
+// Split-KV decode.  One workgroup per (sequence, group of HG adjacent kv heads,
+// run of consecutive chunks), one wave per head; the host sizes the runs so
+// that the grid is resident at once.  The HG heads' slices of a cache row are
+// adjacent in memory, so the workgroup copies whole HG*C-byte row segments
+// HBM -> LDS: every global_load_lds_dwordx4 moves 1 KB of consecutive bytes,
+// and the waves share the copies of a tile equally.  The ring of NS tile slots
+// belongs to the workgroup and runs on across chunk ends; one barrier per tile
+// both publishes the tile whose copies each wave has waited for and frees the
+// slot read in the step before.  At the end of each chunk every wave writes
+// the partial output (not yet multiplied by the value scale, which the combine
+// applies once) and log-sum-exp of its G query heads.
 // ---------------------------------------------------------------------------
-constexpr int kSplitWaves = 8;
+template <int KVF, int D, int HG> struct SplitGeo {
+  static constexpr int C = KvGeom<KVF, D>::C;
+  static constexpr int RB = HG * C;                          // bytes of a row segment
+  static constexpr int RB16 = RB / 16;                       // its 16-byte chunks
+  static constexpr int SWM = (RB16 < 16 ? RB16 : 16) - 1;   // chunk swizzle mask
+  static constexpr int TILE = 64 * RB;                       // 32 K rows + 32 V rows
+  static constexpr int NIW = C / 16;                         // 1 KB copies per wave per tile
+  static constexpr int ROWS_PER_COPY = 64 / RB16;
+  static_assert(RB16 >= 2 && (RB16 & (RB16 - 1)) == 0, "row segment");
+};
 
-template <int D, int KVF, int SM, typename TQ, int NS>
-__global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(
+// LDS offset of byte b of row r's segment inside the K (or V) half of a slot:
+// chunk (b / 16) of row r sits at chunk position (b / 16) ^ (r & SWM).
+template <int KVF, int D, int HG>
+__device__ __forceinline__ int split_off(int r, int b) {
+  using SG = SplitGeo<KVF, D, HG>;
+  return r * SG::RB + 16 * ((b >> 4) ^ (r & SG::SWM)) + (b & 15);
+}
+
+// Copy j (0..NIW-1) of this wave fills slot bytes [1024q, 1024q + 1024) with
+// q = j*HG + wave; its lane l loads the chunk that belongs at chunk position
+// 64q + l of the K rows (q < RB16/2) or of the V rows.
+template <int KVF, int D, int HG> struct SplitCopy {
+  using SG = SplitGeo<KVF, D, HG>;
+  int r[SG::NIW];             // tile row of this lane's chunk, per copy
+  uint32_t lane_off[SG::NIW]; // r * row_stride + 16 * global chunk, per copy
+
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride) {
+#pragma unroll
+    for (int j = 0; j < SG::NIW; ++j) {
+      const int q = j * HG + wave;
+      const int pr = (q % (SG::RB16 / 2)) * 64 + lane;
+      r[j] = pr / SG::RB16;
+      const int gc = (pr % SG::RB16) ^ (r[j] & SG::SWM);
+      lane_off[j] = (uint32_t)r[j] * row_stride + 16u * (uint32_t)gc;
+    }
+  }
+
+  // Queue this wave's copies of the tile at key k0 of a chunk ending at kend.
+  // In a tile cut by the chunk end, rows past it repeat the chunk's last row.
+  __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs, TileOffsets to,
+                                        const uint8_t* kbase, const uint8_t* vbase,
+                                        uint32_t row_stride, int wave) const {
+    const int bmask = (1 << lbs) - 1;
+    const bool full = k0 + 32 <= kend;
+    // k0 is a multiple of 16: key k0 + r sits in row (k0 & bmask) + r of the
+    // block at to.off0 for r < 16, and in row ((k0 + 16) & bmask) + r - 16 of
+    // the block at to.off1 otherwise (the same block when block_size >= 32)
+    const size_t base0 = to.off0 + (size_t)((uint32_t)(k0 & bmask) * row_stride);
+    const size_t base1 = to.off1 + (size_t)((uint32_t)((k0 + 16) & bmask) * row_stride) -
+                         (size_t)(16u * row_stride);
+#pragma unroll
+    for (int j = 0; j < SG::NIW; ++j) {
+      const int q = j * HG + wave;                         // wave-uniform
+      const bool is_v = q >= SG::RB16 / 2;
+      const uint8_t* base = is_v ? vbase : kbase;
+      size_t off;
+      if (full) {
+        off = (r[j] < 16 ? base0 : base1) + lane_off[j];
+      } else {
+        const int rr = r[j];
+        const uint32_t row = (uint32_t)(min(k0 + rr, kend - 1) & bmask);
+        off = (rr < 16 ? to.off0 : to.off1) + row * row_stride +
+              (lane_off[j] - (uint32_t)rr * row_stride);
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base + off),
+          (__attribute__((address_space(3))) void*)(slot + q * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// This wave's (head `wave` of the group) operand bytes of one tile.
+template <int KVF, int D, int HG>
+__device__ __forceinline__ void read_split_tile(const uint8_t* slot, TileRaw<KVF, D>& t,
+                                                int col, int grp, int wave) {
+  using Geo = KvGeom<KVF, D>;
+  using SG = SplitGeo<KVF, D, HG>;
+  constexpr int KB = Geo::KBYTES, C = Geo::C;
+  const int hb = wave * C;                                 // head's first byte in the segment
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 16 * hh + col;
+    if constexpr (KB >= 16) {
+#pragma unroll
+      for (int j = 0; j < KB / 16; ++j)
+        lds_bytes<16>(slot + split_off<KVF, D, HG>(r, hb + KB * grp + 16 * j), &t.kw[hh][4 * j]);
+    } else {
+      lds_bytes<KB>(slot + split_off<KVF, D, HG>(r, hb + KB * grp), t.kw[hh]);
+    }
+  }
+  const uint8_t* vs = slot + 32 * SG::RB;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
+    t.vw[e][1] = 0;
+    lds_bytes<Geo::VBYTES>(vs + split_off<KVF, D, HG>(r, hb + Geo::VBYTES * col), t.vw[e]);
+  }
+}
+
+// Key range of chunk c: blocks [c*nb/S, (c+1)*nb/S) of the sequence.
+// (c * nb stays below 2^32: the host bounds max_blocks_per_seq * num_splits.)
+__device__ __forceinline__ void chunk_keys(int c, int nb, int S, int bs, int kv_len, int& kb,
+                                           int& ke) {
+  kb = (int)(((uint32_t)c * (uint32_t)nb) / (uint32_t)S) * bs;
+  ke = min(kv_len, (int)(((uint32_t)(c + 1) * (uint32_t)nb) / (uint32_t)S) * bs);
+}
+
+// Position of the next tile to copy: chunk pc, key pk (< pke), or pc == c1.
+struct TileCursor {
+  int pc, pk, pke;
+  __device__ __forceinline__ void settle(int c1, int nb, int S, int bs, int kv_len) {
+    while (pc < c1 && pk >= pke) {
+      if (++pc < c1) chunk_keys(pc, nb, S, bs, kv_len, pk, pke);
+    }
+  }
+};
+
+template <int D, int KVF, int SM, typename TQ, int HG, int NS>
+__global__ __launch_bounds__(HG * 64) void decode_split_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
   using Geo = KvGeom<KVF, D>;
-  using R = Ring<KVF, D>;
+  using SG = SplitGeo<KVF, D, HG>;
+  static_assert(NS == 2 || NS == 3, "ring depth");
   constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x * kSplitWaves + wave, b = blockIdx.y, chunk = blockIdx.z;
-  if (h >= a.hkv) return;                                   // no barriers below
+  const int h = blockIdx.x * HG + wave, b = blockIdx.y;
   const int q0 = a.cum_q[b];
   if (a.cum_q[b + 1] == q0) return;                         // no new token: no rows
   const int kv_len = a.past_lens[b] + 1;
@@ -541,74 +682,100 @@ __global__ __launch_bounds__(kSplitWaves * 64) void decode_split_kernel(
   const int G = H / hkv;
   const int nb = (kv_len + bs - 1) / bs;
   const int S = a.num_splits;
-  const int kbeg = (int)(((long)chunk * nb) / S) * bs;
-  const int kend = min(kv_len, (int)(((long)(chunk + 1) * nb) / S) * bs);
+  const int c0 = blockIdx.z * a.split_chunks_per_wg;
+  const int c1 = min(S, c0 + a.split_chunks_per_wg);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
   const int lbs = a.block_size_log2;
   const uint32_t row_stride = (uint32_t)(hkv * C);
-  const uint8_t* kbase = a.key_cache + (size_t)h * C;
-  const uint8_t* vbase = a.value_cache + (size_t)h * C;
+  const uint8_t* kbase = a.key_cache + (size_t)blockIdx.x * SG::RB;
+  const uint8_t* vbase = a.value_cache + (size_t)blockIdx.x * SG::RB;
 
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kSplitWaves][NS * R::SLOT];
-  uint8_t* myring = ring[wave];
-  if (kbeg < kend) {
+  // query and key-scale loads go out before the tile copies
+  QueryRaw<D, SM> qraw;
+  load_query<D, SM, TQ>(a, h, q0, G, col, grp, qraw);
+  __builtin_amdgcn_sched_barrier(0);
+
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SG::TILE];
+  SplitCopy<KVF, D, HG> cp;
+  cp.init(wave, lane, row_stride);
+  TileCursor pcur;
+  pcur.pc = c0;
+  chunk_keys(c0, nb, S, bs, kv_len, pcur.pk, pcur.pke);
+  pcur.settle(c1, nb, S, bs, kv_len);
+  int issued = 0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      issue_tile<KVF, D>(myring + j * R::SLOT, kbeg + 32 * j, kend, lbs,
-                         tile_offsets(kbeg + 32 * j, kend, lbs, table, row_stride), kbase, vbase,
-                         row_stride, lane);
+  for (int j = 0; j < NS - 1; ++j) {
+    if (pcur.pc < c1) {
+      cp.issue(ring + j * SG::TILE, pcur.pk, pcur.pke, lbs,
+               tile_offsets(pcur.pk, pcur.pke, lbs, table, row_stride), kbase, vbase, row_stride,
+               wave);
+      ++issued;
+      pcur.pk += 32;
+      pcur.settle(c1, nb, S, bs, kv_len);
+    }
   }
+  TileOffsets nxt = tile_offsets(pcur.pc < c1 ? pcur.pk : 0, pcur.pc < c1 ? pcur.pke : 1, lbs,
+                                 table, row_stride);
+  __builtin_amdgcn_sched_barrier(0);
+
   f16x8 qhi[NQK], qlo[NQK];
   float Mh;
-  fold_query<D, KVF, SM, TQ>(a, h, q0, G, col, grp, qhi, qlo, Mh);
+  fold_loaded_query<D, KVF, SM, TQ>(qraw, qhi, qlo, Mh);
   const float c2 = a.softmax_scale * Mh * kLog2e;
 
-  WaveState<D> st;
+  int consumed = 0, cur = 0;
+  for (int c = c0; c < c1; ++c) {
+    int kb, ke;
+    chunk_keys(c, nb, S, bs, kv_len, kb, ke);
+    WaveState<D> st;
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  if (kbeg < kend) {
-    int cur = 0;
-    TileOffsets nxt = tile_offsets(kbeg + 32 * NS, kend, lbs, table, row_stride);
-    for (int k = kbeg; k < kend; k += 32) {
+    for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int k = kb; k < ke; k += 32) {
+      // this wave's copies of the tile are done (those of the next may fly)
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt_le((NS - 1) * 2 * R::NI);
+      if (NS == 3 && issued - consumed > 1) wait_vmcnt_le<SG::NIW>();
+      else wait_vmcnt_le<0>();
+      // every wave's copies of the tile are done, and every wave has read the
+      // slot about to be refilled
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t* slot = myring + cur * R::SLOT;
-      TileRaw<KVF, D> t;
-      read_tile<KVF, D>(slot, t, col, grp);
-      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+      if (pcur.pc < c1) {
+        cp.issue(ring + ((cur + NS - 1) % NS) * SG::TILE, pcur.pk, pcur.pke, lbs, nxt, kbase,
+                 vbase, row_stride, wave);
+        ++issued;
+        pcur.pk += 32;
+        pcur.settle(c1, nb, S, bs, kv_len);
+        if (pcur.pc < c1) nxt = tile_offsets(pcur.pk, pcur.pke, lbs, table, row_stride);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      issue_tile<KVF, D>(slot, k + 32 * NS, kend, lbs, nxt, kbase, vbase, row_stride, lane);
-      nxt = tile_offsets(k + 32 * (NS + 1), kend, lbs, table, row_stride);
+      TileRaw<KVF, D> tr;
+      read_split_tile<KVF, D, HG>(ring + cur * SG::TILE, tr, col, grp, wave);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): slot reads done
       __builtin_amdgcn_sched_barrier(0);
-      compute_tile<KVF, D>(t, k, kend, c2, qhi, qlo, st, grp);
+      compute_tile<KVF, D>(tr, k, ke, c2, qhi, qlo, st, grp);
+      ++consumed;
       cur = (cur + 1 == NS) ? 0 : cur + 1;
     }
-  }
-  wait_vmcnt_le(0);
-
-  // normalised partial output and log-sum-exp of this wave's G query heads
-  const float L = rows_sum(st.l);
-  if (col < G) {
-    const int hq = h * G + col;
-    const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
-    const float inv = (L > 0.f) ? 1.f / L : 0.f;            // both carry 2^7
-    float* po = a.part_o + pi * D;
+    // partial output (value scale not applied) and log-sum-exp of chunk c
+    const float L = rows_sum(st.l);
+    if (col < G) {
+      const int hq = h * G + col;
+      const size_t pi = ((size_t)q0 * H + hq) * S + c;
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;          // both carry 2^7
+      float* po = a.part_o + pi * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d0 = (D / 16) * (4 * grp + r);
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = (D / 16) * (4 * grp + r);
 #pragma unroll
-      for (int nbk = 0; nbk < NPV; ++nbk) {
-        const int d = d0 + nbk;
-        const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
-        po[d] = st.o[nbk][r] * inv * vs;
+        for (int nbk = 0; nbk < NPV; ++nbk) po[d0 + nbk] = st.o[nbk][r] * inv;
       }
+      if (grp == 0)
+        a.part_lse[pi] = (L > 0.f) ? (st.m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
     }
-    if (grp == 0)
-      a.part_lse[pi] = (L > 0.f) ? (st.m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
   }
+  wait_vmcnt_le<0>();
 }
 
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype) {
@@ -618,7 +785,7 @@ bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype)
 
 template <int D, int KVF, int SM, int NW, int NS, int HP>
 static int launch_dqw(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.hkv / HP, a.batch, a.num_splits);
+  dim3 grid(a.hkv / HP, a.batch, 1);
   if (a.q_dtype == DT_F16)
     hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16, NW, NS, HP>), grid, dim3(NW * 64), 0,
                        st, a, a.block_table);
@@ -630,22 +797,46 @@ static int launch_dqw(const AttnArgs& a, hipStream_t st) {
   return 0;
 }
 
-// Waves per workgroup: enough tiles per wave to amortise the set-up, and at
-// most one tile per wave per 256-key chunk of split decode.  Rows shorter than
-// a 128-byte line (packed INT4 with D=128, any format with D=64) pair two kv
-// heads per workgroup when the head count allows.
+// Split-KV: HG = the largest of 8, 4, 2, 1 that divides the kv head count.
+// Each workgroup takes a run of consecutive chunks, sized so that the whole
+// grid is resident at once.
+template <typename K>
+static int resident_wgs_per_cu(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+template <int D, int KVF, int SM, typename TQ, int HG>
+static int launch_split_hg_q(const AttnArgs& a0, hipStream_t st) {
+  constexpr int NS = (3 * SplitGeo<KVF, D, HG>::TILE <= 160 * 1024) ? 3 : 2;
+  auto kernel = decode_split_kernel<D, KVF, SM, TQ, HG, NS>;
+  static int per_cu = 0;                                  // kernel property: same on every call
+  if (per_cu == 0) per_cu = resident_wgs_per_cu(kernel, HG * 64);
+  AttnArgs a = a0;
+  const long units = (long)(a.hkv / HG) * a.batch * a.num_splits;
+  const long slots = (long)(a.num_cus > 0 ? a.num_cus : 256) * per_cu;
+  a.split_chunks_per_wg = (int)((units + slots - 1) / slots);
+  const int runs = (a.num_splits + a.split_chunks_per_wg - 1) / a.split_chunks_per_wg;
+  dim3 grid(a.hkv / HG, a.batch, runs);
+  hipLaunchKernelGGL(kernel, grid, dim3(HG * 64), 0, st, a, a.block_table);
+  return 0;
+}
+
+template <int D, int KVF, int SM, int HG>
+static int launch_split_hg(const AttnArgs& a, hipStream_t st) {
+  if (a.q_dtype == DT_F16) return launch_split_hg_q<D, KVF, SM, f16, HG>(a, st);
+  if (a.q_dtype == DT_BF16) return launch_split_hg_q<D, KVF, SM, bf16, HG>(a, st);
+  return -1;
+}
+
 template <int D, int KVF, int SM>
 static int launch_split(const AttnArgs& a, hipStream_t st) {
-  dim3 grid((a.hkv + kSplitWaves - 1) / kSplitWaves, a.batch, a.num_splits);
-  if (a.q_dtype == DT_F16)
-    hipLaunchKernelGGL((decode_split_kernel<D, KVF, SM, f16, 2>), grid, dim3(kSplitWaves * 64), 0,
-                       st, a, a.block_table);
-  else if (a.q_dtype == DT_BF16)
-    hipLaunchKernelGGL((decode_split_kernel<D, KVF, SM, bf16, 2>), grid, dim3(kSplitWaves * 64),
-                       0, st, a, a.block_table);
-  else
-    return -1;
-  return 0;
+  if (a.hkv % 8 == 0) return launch_split_hg<D, KVF, SM, 8>(a, st);
+  if (a.hkv % 4 == 0) return launch_split_hg<D, KVF, SM, 4>(a, st);
+  if (a.hkv % 2 == 0) return launch_split_hg<D, KVF, SM, 2>(a, st);
+  return launch_split_hg<D, KVF, SM, 1>(a, st);
 }
 
 // Single pass: one workgroup per (sequence, kv head) whose waves take the

@@ -101,12 +101,28 @@ __device__ __forceinline__ f16x2 i8pair_to_f16x2(uint32_t x_biased, uint32_t sel
   return v - (f16x2){(f16)1152.0f, (f16)1152.0f};
 }
 
-// Nibbles (already XOR-ed with 0x8, so u = code + 8) at bits [0,4) and
-// [16,20) of x >> shift -> fp16 pair.
-__device__ __forceinline__ f16x2 nib_to_f16x2(uint32_t x_biased, int shift) {
-  uint32_t m = ((x_biased >> shift) & 0x000F000Fu) | 0x64006400u;
-  f16x2 v = bitcast<f16x2>(m);
-  return v - (f16x2){(f16)1032.0f, (f16)1032.0f};
+// Eight packed INT4 codes (two's-complement nibbles; nibble k of w is code k)
+// -> four exact fp16 pairs o[0] = (c0, c4), o[1] = (c1, c5), o[2] = (c2, c6),
+// o[3] = (c3, c7).  One v_bitop3 per pair computes, bit by bit,
+// mask ? (w ^ k) : k, with k holding the 0x6400 exponent outside the nibble
+// fields and the nibble's sign bit inside them: that places u = code + 8 in the
+// mantissa of 1024.0 (nibbles 0, 2, 4, 6: value 1024 + u) or 16u there
+// (nibbles 1, 3, 5, 7: value 1024 + 16u, scaled back by an exact fma).
+__device__ __forceinline__ void int4x8_to_f16x2x4(uint32_t w, f16x2 (&o)[4]) {
+  // truth table of (S1 ? S0 ^ S2 : S2) with S0, S1, S2 = 0xF0, 0xCC, 0xAA
+  constexpr uint32_t kMaskedXor = 0x6A;
+  const uint32_t w8 = w >> 8;
+  const uint32_t p0 = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, kMaskedXor);
+  const uint32_t p1 = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, kMaskedXor);
+  const uint32_t p2 = __builtin_amdgcn_bitop3_b32(w8, 0x000F000Fu, 0x64086408u, kMaskedXor);
+  const uint32_t p3 = __builtin_amdgcn_bitop3_b32(w8, 0x00F000F0u, 0x64806480u, kMaskedXor);
+  const f16x2 lo_bias = (f16x2){(f16)-1032.0f, (f16)-1032.0f};
+  const f16x2 hi_scale = (f16x2){(f16)0.0625f, (f16)0.0625f};
+  const f16x2 hi_bias = (f16x2){(f16)-72.0f, (f16)-72.0f};
+  o[0] = bitcast<f16x2>(p0) + lo_bias;
+  o[1] = __builtin_elementwise_fma(bitcast<f16x2>(p1), hi_scale, hi_bias);
+  o[2] = bitcast<f16x2>(p2) + lo_bias;
+  o[3] = __builtin_elementwise_fma(bitcast<f16x2>(p3), hi_scale, hi_bias);
 }
 
 // E4M3 bytes placed at bits [8,16) and [24,32) of y -> fp16 pair (exact):

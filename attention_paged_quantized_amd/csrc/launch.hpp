@@ -43,6 +43,8 @@ struct AttnArgs {
   int max_query_len;    // exact, from the host cum_q
   int max_kv_len;       // longest sequence with new rows (host)
   int block_size_log2;  // block_size is a power of two
+  int num_cus;          // compute units of the device (split-KV grid sizing)
+  int split_chunks_per_wg;  // split-KV: consecutive chunks per workgroup (set by the launcher)
   float softmax_scale;  // already resolved (> 0)
 };
 

@@ -167,6 +167,11 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
     }
   }
   if (S > 4096) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d > 4096", S);
+  // chunk bounds are computed as chunk * blocks / num_splits in 32-bit unsigned
+  if (S > 1 && (unsigned long long)(S + 1) * (unsigned long long)d->max_blocks_per_seq >=
+                   (1ull << 32))
+    return fail(PAQ_ERR_UNSUPPORTED, "num_splits %d x max_blocks_per_seq %d too large", S,
+                d->max_blocks_per_seq);
   p->num_splits = S;
   if (mfma) {
     p->path = S > 1 ? PAQ_PATH_SPLIT : PAQ_PATH_SINGLE;
@@ -330,6 +335,8 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
   paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
                               block_table, cum_q, past_lens, softmax_scale, p);
   if (p.num_splits > 1) {
+    rc = device_cu_count(&a.num_cus);
+    if (rc) return rc;
     const size_t rows = (size_t)d->token_count * d->num_heads * p.num_splits;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
