@@ -48,6 +48,17 @@ def parse():
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--skip-warm", action="store_true",
+                    help="skip the cache-warm reference calls (profiler runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run the plain copy kernel that scales HBM counters")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="no GPU: turn a rocprofv3 --stats kernel_stats.csv into a "
+                         "profiles/ summary for --workload and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then "
+                         "WRITE_SIZE) into profiles/counters_<workload>.json and exit")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     return ap.parse_args()
 
 
@@ -74,10 +85,11 @@ def source_sha(kind):
 def counters(workload, kind, launch_bytes):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
-    if not os.path.exists(path):
+    import glob
+    found = glob.glob(os.path.join(ROOT, "profiles", "*_%s_counters.json" % workload))
+    if len(found) != 1:
         return None
-    with open(path) as f:
+    with open(found[0]) as f:
         c = json.load(f)
     if c.get("source_sha") != source_sha(kind):
         return None
@@ -128,8 +140,121 @@ def cpu_baseline(w, seconds):
     return res
 
 
+# Kernels of one attention call, by workload kind (substrings of the symbol).
+CALL_KERNELS = {"decode": ("decode_mfma_kernel", "decode_split_kernel", "combine_kernel",
+                           "attn_f32_kernel"),
+                "prefill": ("prefill_mfma_kernel", "attn_f32_kernel")}
+CALIB_KERNEL = "neg_kernel"
+
+
+def _short(name):
+    for k in ("decode_mfma_kernel", "decode_split_kernel", "combine_kernel", "attn_f32_kernel",
+              "prefill_mfma_kernel", "quant_append_kernel", CALIB_KERNEL):
+        if k in name:
+            return k
+    return name[:48]
+
+
+def summarize_stats(args):
+    """rocprofv3 --kernel-trace --stats CSV -> profiles/<kernel>_<workload>.txt"""
+    import csv
+    import workloads
+    w = workloads.make(args.workload)
+    rows = list(csv.DictReader(open(args.summarize_stats)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    call = [r for r in rows if any(k in r["Name"] for k in CALL_KERNELS[w.kind])]
+    main_k = _short(call[0]["Name"]) if call else "none"
+    lines = ["rocprofv3 kernel statistics, workload %s (%s)" % (w.name, w.kind),
+             "command: %s" % (args.command or "(not recorded)"),
+             "kernel sources sha256[:16]: %s" % source_sha(w.kind), "",
+             "%-22s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us",
+                                                 "max_us", "total_us")]
+    for r in rows[:12]:
+        lines.append("%-22s %7d %12.3f %12.3f %12.3f %12.1f" % (
+            _short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3))
+    tot = sum(float(r["AverageNs"]) for r in call) / 1e3
+    lines += ["", "attention call (%s): %.3f us average per call" %
+              (" + ".join(_short(r["Name"]) for r in call), tot)]
+    if w.kind == "decode":
+        kvb = kv_bytes(w)
+        lines.append("algorithmic KV bytes per call %d -> %.1f GB/s, %.4f of 8000 GB/s" %
+                     (kvb, kvb / (tot * 1e3), kvb / (tot * 1e3) / HBM_PEAK_GBS))
+    else:
+        fl = prefill_flops(w)
+        lines.append("algorithmic flops per call %d -> %.1f TFLOP/s, %.4f of %.1f" %
+                     (fl, fl / (tot * 1e-6) / 1e12, fl / (tot * 1e-6) / 1e12 /
+                      MFMA_PEAK_TFLOPS[w.q_dtype], MFMA_PEAK_TFLOPS[w.q_dtype]))
+    out = os.path.join(ROOT, "profiles", "%s_%s.txt" % (main_k, w.name))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
+def summarize_pmc(args):
+    """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) -> per-call HBM bytes of
+    the attention kernels, scaled by the counters of a 256 MiB copy, written to
+    profiles/counters_<workload>.json"""
+    import csv
+    import glob
+    import workloads
+    w = workloads.make(args.workload)
+
+    def medians(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+
+    fetch = medians(args.summarize_pmc[0], "FETCH_SIZE")
+    write = medians(args.summarize_pmc[1], "WRITE_SIZE")
+    calib_kib = CALIB_ELEMS * 4 / 1024.0
+    ff = calib_kib / fetch[CALIB_KERNEL]
+    wf = calib_kib / write[CALIB_KERNEL]
+    ks = [k for k in CALL_KERNELS[w.kind] if k in fetch]
+    res = {"workload": w.name, "source_sha": source_sha(w.kind), "command": args.command,
+           "calibration": "torch.neg over %d fp32 (%.0f KiB read, %.0f KiB written): "
+                          "FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" %
+                          (CALIB_ELEMS, calib_kib, calib_kib, fetch[CALIB_KERNEL],
+                           write[CALIB_KERNEL]),
+           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+           "kernels": {k: {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0)} for k in ks},
+           "fetch_kib": sum(fetch[k] for k in ks), "write_kib": sum(write.get(k, 0.0) for k in ks)}
+    hbm = (res["fetch_kib"] * ff + res["write_kib"] * wf) * 1024
+    res["hbm_bytes_per_call"] = int(hbm)
+    if w.kind == "decode":
+        res["algorithmic_kv_bytes_per_call"] = kv_bytes(w)
+        res["traffic_over_algorithmic"] = round(hbm / kv_bytes(w), 4)
+    out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (ks[0], w.name))
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print("wrote", out, json.dumps(res))
+
+
+CALIB_ELEMS = 2 ** 26          # fp32 elements of the counter-calibration copy (256 MiB)
+
+
+def sleep_rate(stream):
+    """Cycles per second of torch.cuda._sleep on this device."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(2_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 2_000_000 / (e0.elapsed_time(e1) / 1e3)
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -189,14 +314,26 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    # Warm up, and measure how long the host takes to queue one step.
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
     for i in range(args.warmup):
         step(i)
+    host_ms = (time.perf_counter() - h0) * 1e3 / max(1, args.warmup)
     torch.cuda.synchronize()
+    hz = sleep_rate(stream)
+
+    def hold(n_steps):
+        # keep the stream busy while the host queues n_steps, so that the
+        # events below time the GPU and not the Python launch rate
+        torch.cuda._sleep(int((2.0 * n_steps * host_ms + 2.0) * 1e-3 * hz))
+
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold(args.steps)
     t_start.record(stream)
     for i in range(args.steps):
         step(i, evs[i])
@@ -209,18 +346,23 @@ def main():
     kern_sorted = sorted(kern_ms)
 
     # warm (cache-resident) reference: the same pool every call, per-call events
-    for i in range(5):
+    warm_ms = None
+    for i in range(0 if args.skip_warm else 5):
         attention(devs[0], outs[0])
     wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(20)]
+           for _ in range(0 if args.skip_warm else 20)]
+    torch.cuda.synchronize()
+    hold(len(wev))
     for e0, e1 in wev:
         e0.record(stream)
         attention(devs[0], outs[0])
         e1.record(stream)
     torch.cuda.synchronize()
-    warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
+    if wev:
+        warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
 
-    # plain streaming copy of 1 GiB for context (read + write bytes / time)
+    # plain streaming copy of 1 GiB for context (read + write bytes / time); with
+    # --calib-copy also the 256 MiB copy whose counters scale FETCH/WRITE_SIZE
     src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -231,6 +373,10 @@ def main():
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    if args.calib_copy:
+        for _ in range(3):
+            torch.neg(src[:CALIB_ELEMS], out=dst[:CALIB_ELEMS])
+        torch.cuda.synchronize()
     del src, dst
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -261,7 +407,7 @@ def main():
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
                               "kernel_us_p10_p90": [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
                                                     round(kern_sorted[9 * len(kern_ms) // 10] * 1e3, 3)],
-                              "warm_cache_us": round(warm_ms * 1e3, 3),
+                              "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
                               "algorithmic_bytes_per_launch": kvb}
     else:
         fl = prefill_flops(w)
@@ -274,7 +420,7 @@ def main():
                               "traffic": counters(w.name, "prefill", fl),
                               "kernel": "paged_attn_prefill call (prefill_mfma)",
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
-                              "warm_cache_us": round(warm_ms * 1e3, 3),
+                              "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
                               "algorithmic_flops_per_launch": fl}
         cfg.update({"max_query_len": int(w.q_lens.max()), "causal": True})
     result["config"] = cfg
