@@ -1,13 +1,15 @@
 // decode_mfma.hip -- GQA paged decode over an INT8 / packed-INT4 / FP8 cache on
 // gfx950 matrix cores (v_mfma_f32_16x16x32_f16), single pass or split-KV.
 //
-// Work unit: one workgroup per (kv head h, sequence b, KV chunk c); its waves
-// take 32-key tiles of the chunk in turn, each with its own online softmax, and
-// merge through LDS at the end.  Decode is HBM-bound (every K/V byte is read
-// once -- "GQA GEMV decode", why-it-is-good item 1), so the design streams the
-// raw codes HBM -> LDS with whole-line non-temporal DMA copies, reads each
-// lane's operand bytes from there and converts them in registers; nothing is
-// ever written back or repacked:
+// Work unit: a wave streams the 32-key tiles of a key range for HW adjacent kv
+// heads (HW = 128 / row bytes, so every copied row segment is a whole 128-byte
+// line) with its own online softmax.  Single pass: the 8 waves of a
+// workgroup share one (sequence, head group) and merge through LDS at the end;
+// split-KV: each wave owns one chunk and writes partials for the combine.
+// Decode is HBM-bound (every K/V byte is read once -- "GQA GEMV decode",
+// why-it-is-good item 1), so the design streams the raw codes HBM -> LDS with
+// whole-line non-temporal DMA copies, reads each lane's operand bytes from
+// there and converts them in registers; nothing is written back or repacked:
 //
 // * QK^T: A = a 16-key x 32-channel tile of K (lane l: key l%16, 8 channels of
 //   its row), B = the folded query Q'^T (lane l: query column l%16).  The
@@ -22,11 +24,12 @@
 //   exactly the B-operand layout of the PV MFMA if its 32-key K dimension is
 //   ordered as {4q..4q+3, 16+4q..16+4q+3} per lane group: no cross-lane moves.
 // * PV: A = V^T (lane dd+16q: 8 keys x channel (D/16)*dd + nb), B = P^T in fp16
-//   scaled by 2^15 (keeps small probabilities normal; "INT8-KV Tensor-Core
+//   scaled by 2^7 (keeps small probabilities normal; "INT8-KV Tensor-Core
 //   DynamicSparseAttention", why-it-is-good item 2), fp32 accumulation.
 // * Online softmax in fp32 (exp2 with the log2(e) factor folded into the
-//   score scale); the rescale of the accumulators is skipped when no lane's
-//   running maximum moved.
+//   score scale).  The running maximum is refreshed lazily: only when a score
+//   exceeds it by more than 2^8 are the maxima exchanged and the accumulators
+//   rescaled, so P stays <= 2^15, inside fp16 range.
 // * Split-KV ("flash decoding", "GQA GEMV decode" section 2): chunk c covers
 //   blocks [c*nb/S, (c+1)*nb/S) of the sequence and writes the normalised
 //   partial output and its log-sum-exp for the combine kernel.
@@ -134,27 +137,32 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vw)[8][2], f16x8 (&v
 }
 
 // ---------------------------------------------------------------------------
-// Streaming through LDS.  Every wave owns a private ring of two tile slots.
-// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane
-// straight into LDS, no registers held while in flight), two tiles ahead of the
-// one being computed.  A slot holds the 32 K rows then the 32 V rows of one
-// tile, row-major; the 16-byte chunks of row r are stored XOR-swizzled by
-// (r mod chunks-per-row) so that the operand reads below are free of bank
-// conflicts.  The compiler does not track LDS-DMA completion, so the kernel
-// waits on vmcnt itself (in-order completion of vector memory loads).
+// Streaming through LDS.  Every wave owns a private ring of NS tile slots and
+// streams its own key range, so no wave ever waits for another while keys are
+// being read.  A wave serves HW adjacent kv heads: their HW * C bytes of a
+// token row are adjacent in the cache, and HW = 128 / C makes that a whole
+// 128-byte line.  Tiles of 32 tokens are copied HBM -> LDS with
+// global_load_lds_dwordx4 (16 bytes per lane straight into LDS, no registers
+// held while in flight): each copy instruction moves 1 KB, i.e. RPI whole row
+// segments of RB bytes, CH lanes per segment.  A slot holds the 32 K row
+// segments then the 32 V row segments of a tile; the 16-byte chunks of row r
+// are stored XOR-swizzled by (r mod chunks-per-row) so that the operand reads
+// are free of bank conflicts.  The compiler does not track LDS-DMA completion,
+// so the kernel waits on vmcnt itself (vector memory loads complete in order).
 // ---------------------------------------------------------------------------
-template <int KVF, int D> struct Ring {
-  using Geo = KvGeom<KVF, D>;
-  static constexpr int C = Geo::C;
-  static constexpr int CH = C / 16;             // 16-byte chunks per row
-  static constexpr int RPI = 64 / CH;           // rows per DMA instruction
-  static constexpr int NI = 32 / RPI;           // DMA instructions per 32 rows
-  static constexpr int SLOT = 64 * C;           // K rows + V rows
+template <int KVF, int D, int HW> struct StreamGeo {
+  static constexpr int C = KvGeom<KVF, D>::C;   // bytes of one head's row
+  static constexpr int RB = HW * C;             // bytes of the wave's row segment
+  static constexpr int CH = RB / 16;            // 16-byte chunks per segment
+  static constexpr int RPI = 64 / CH;           // segments per copy instruction
+  static constexpr int NI = 32 / RPI;           // copy instructions per 32 rows
+  static constexpr int SLOT = 64 * RB;          // K rows + V rows of one tile
+  static_assert(CH >= 2 && CH <= 8 && (CH & (CH - 1)) == 0, "row segment");
 };
 
-// Cache policy of the streaming copies: non-temporal.  Every K/V byte is
-// read exactly once per call, and the hint measurably raises the achieved HBM
-// rate of these whole-line (8 lanes x 16 B per 128-byte row) copies.
+// Cache policy of the streaming copies: non-temporal.  Every K/V byte is read
+// exactly once per call, and with whole-line copies the hint measurably raises
+// the achieved HBM rate.
 constexpr int kNonTemporal = 2;
 
 template <int N>
@@ -165,57 +173,67 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Queue the copy of the tile starting at key k0 into `slot` (wave-uniform).
-// Keys past the chunk end are clamped to its last key (a valid row).
-struct TileOffsets {
-  size_t off0, off1;   // byte offsets of the physical blocks of the two 16-key halves
+// LDS offset of byte b of row r's segment inside the K (or V) half of a slot.
+template <int KVF, int D, int HW>
+__device__ __forceinline__ int stream_off(int r, int b) {
+  using SG = StreamGeo<KVF, D, HW>;
+  return r * SG::RB + 16 * ((b >> 4) ^ (r % SG::CH)) + (b & 15);
+}
+
+// One wave's copies of its tiles.  Copy instruction i of a half-tile (K or V)
+// fills slot bytes [1024 i, 1024 i + 1024); lane l of it loads the global
+// chunk that belongs at chunk position l % CH of tile row RPI*i + l / CH.
+template <int KVF, int D, int HW> struct WaveCopy {
+  using SG = StreamGeo<KVF, D, HW>;
+  uint32_t lane_off[SG::NI];   // row * row_stride + 16 * global chunk, per instruction
+  int row[SG::NI];             // tile row of this lane's chunk, per instruction
+
+  __device__ __forceinline__ void init(int lane, uint32_t row_stride) {
+#pragma unroll
+    for (int i = 0; i < SG::NI; ++i) {
+      const int r = SG::RPI * i + lane / SG::CH;
+      row[i] = r;
+      lane_off[i] = (uint32_t)r * row_stride + 16u * (uint32_t)((lane % SG::CH) ^ (r % SG::CH));
+    }
+  }
+
+  // Queue the copy of the tile at key k0 (a multiple of 32) of a key range
+  // ending at kend into `slot`.  Rows at or past kend repeat row kend - 1 (a
+  // valid row; their scores are masked).  Each 16-key half of the tile lies in
+  // one physical block (block_size is a multiple of 16, and of 32 when a block
+  // holds both halves).
+  __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs,
+                                        const int32_t* __restrict__ table, const uint8_t* kbase,
+                                        const uint8_t* vbase, uint32_t row_stride) const {
+    const int bmask = (1 << lbs) - 1;
+    const size_t blk0 = (size_t)table[min(k0, kend - 1) >> lbs] << lbs;
+    const size_t blk1 = (size_t)table[min(k0 + 16, kend - 1) >> lbs] << lbs;
+    // key k0 + r sits in row (k0 & bmask) + r of block blk0 for r < 16 and in
+    // row ((k0 + 16) & bmask) + r - 16 of block blk1 otherwise
+    const size_t base0 = (blk0 + (size_t)(k0 & bmask)) * row_stride;
+    const size_t base1 = (blk1 + (size_t)((k0 + 16) & bmask)) * row_stride - 16 * (size_t)row_stride;
+    const bool full = k0 + 32 <= kend;
+#pragma unroll
+    for (int i = 0; i < SG::NI; ++i) {
+      size_t off;
+      if (full) {
+        off = (row[i] < 16 ? base0 : base1) + lane_off[i];
+      } else {
+        const int r = row[i];
+        const uint32_t rr = (uint32_t)(min(k0 + r, kend - 1) & bmask);
+        off = ((r < 16 ? blk0 : blk1) + rr) * row_stride +
+              (lane_off[i] - (uint32_t)r * row_stride);
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kbase + off),
+          (__attribute__((address_space(3))) void*)(slot + i * 1024), 16, 0, kNonTemporal);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + off),
+          (__attribute__((address_space(3))) void*)(slot + 32 * SG::RB + i * 1024), 16, 0,
+          kNonTemporal);
+    }
+  }
 };
-
-__device__ __forceinline__ TileOffsets tile_offsets(int k0, int kend, int lbs,
-                                                    const int32_t* __restrict__ table,
-                                                    uint32_t row_stride) {
-  TileOffsets t;
-  t.off0 = ((size_t)table[min(k0, kend - 1) >> lbs] << lbs) * row_stride;
-  t.off1 = ((size_t)table[min(k0 + 16, kend - 1) >> lbs] << lbs) * row_stride;
-  return t;
-}
-
-template <int KVF, int D>
-__device__ __forceinline__ void issue_tile(uint8_t* slot, int k0, int kend, int lbs,
-                                           TileOffsets to, const uint8_t* kbase,
-                                           const uint8_t* vbase, uint32_t row_stride, int lane) {
-  using R = Ring<KVF, D>;
-  const int bmask = (1 << lbs) - 1;
-  const size_t off0 = to.off0, off1 = to.off1;
-  const int c = lane % R::CH;
-#pragma unroll
-  for (int i = 0; i < R::NI; ++i) {
-    const int r = R::RPI * i + lane / R::CH;
-    const uint32_t row = (uint32_t)(min(k0 + r, kend - 1) & bmask);
-    const uint32_t lane_off = row * row_stride + 16u * (uint32_t)(c ^ (r % R::CH));
-    const size_t off = (r < 16) ? off0 : off1;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(kbase + off + lane_off),
-        (__attribute__((address_space(3))) void*)(slot + i * 1024), 16, 0, kNonTemporal);
-  }
-#pragma unroll
-  for (int i = 0; i < R::NI; ++i) {
-    const int r = R::RPI * i + lane / R::CH;
-    const uint32_t row = (uint32_t)(min(k0 + r, kend - 1) & bmask);
-    const uint32_t lane_off = row * row_stride + 16u * (uint32_t)(c ^ (r % R::CH));
-    const size_t off = (r < 16) ? off0 : off1;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(vbase + off + lane_off),
-        (__attribute__((address_space(3))) void*)(slot + 32 * R::C + i * 1024), 16, 0, kNonTemporal);
-  }
-}
-
-// Byte offset of byte b of row r inside a K or V block of a slot.
-template <int KVF, int D>
-__device__ __forceinline__ int slot_off(int r, int b) {
-  using R = Ring<KVF, D>;
-  return r * R::C + 16 * ((b >> 4) ^ (r % R::CH)) + (b & 15);
-}
 
 template <int NB>
 __device__ __forceinline__ void lds_bytes(const uint8_t* p, uint32_t* w) {
@@ -233,35 +251,38 @@ __device__ __forceinline__ void lds_bytes(const uint8_t* p, uint32_t* w) {
   }
 }
 
-// One tile's operand bytes for this lane, read from a slot.
+// One tile's operand bytes of head hh (0..HW-1) of the wave's segment, for
+// this lane, read from a slot.
 template <int KVF, int D> struct TileRaw {
   uint32_t kw[2][KvGeom<KVF, D>::KDW];   // K: key col of each 16-key half, segment grp
   uint32_t vw[8][2];                      // V: keys {4grp+r, 16+4grp+r}, channels (D/16)*col..
 };
 
-template <int KVF, int D>
+template <int KVF, int D, int HW>
 __device__ __forceinline__ void read_tile(const uint8_t* slot, TileRaw<KVF, D>& t, int col,
-                                          int grp) {
+                                          int grp, int hh) {
   using Geo = KvGeom<KVF, D>;
-  using R = Ring<KVF, D>;
+  using SG = StreamGeo<KVF, D, HW>;
   constexpr int KB = Geo::KBYTES;
+  const int hb = hh * Geo::C;                              // head's first byte in the segment
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = 16 * hh + col;
+  for (int half = 0; half < 2; ++half) {
+    const int r = 16 * half + col;
     if constexpr (KB >= 16) {
 #pragma unroll
       for (int j = 0; j < KB / 16; ++j)
-        lds_bytes<16>(slot + slot_off<KVF, D>(r, KB * grp + 16 * j), &t.kw[hh][4 * j]);
+        lds_bytes<16>(slot + stream_off<KVF, D, HW>(r, hb + KB * grp + 16 * j),
+                      &t.kw[half][4 * j]);
     } else {
-      lds_bytes<KB>(slot + slot_off<KVF, D>(r, KB * grp), t.kw[hh]);
+      lds_bytes<KB>(slot + stream_off<KVF, D, HW>(r, hb + KB * grp), t.kw[half]);
     }
   }
-  const uint8_t* vs = slot + 32 * R::C;
+  const uint8_t* vs = slot + 32 * SG::RB;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int r = e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
     t.vw[e][1] = 0;
-    lds_bytes<Geo::VBYTES>(vs + slot_off<KVF, D>(r, Geo::VBYTES * col), t.vw[e]);
+    lds_bytes<Geo::VBYTES>(vs + stream_off<KVF, D, HW>(r, hb + Geo::VBYTES * col), t.vw[e]);
   }
 }
 
@@ -429,232 +450,6 @@ __device__ __forceinline__ void fold_query(const AttnArgs& a, int h, int q0, int
   fold_loaded_query<D, KVF, SM, TQ>(r, qhi, qlo, Mh);
 }
 
-template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HP>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(AttnArgs a,
-                                                             const int32_t* __restrict__ block_table) {
-  using Geo = KvGeom<KVF, D>;
-  using R = Ring<KVF, D>;
-  constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
-  // HP kv heads per workgroup (2 when a head's cache row is shorter than a
-  // 128-byte line: both heads' halves of every line are then read by the
-  // same CU); NW / HP waves per head
-  constexpr int NWH = NW / HP;
-  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x * HP + wave_all / NWH, b = blockIdx.y;
-  const int q0 = a.cum_q[b];
-  if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
-  const int kv_len = a.past_lens[b] + 1;
-  const int hkv = a.hkv, H = a.num_heads;
-  const int G = H / hkv;
-  const int kbeg = 0, kend = kv_len;
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_all % NWH;                          // wave index within its head
-  const int col = lane & 15, grp = lane >> 4;
-  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
-  const int lbs = a.block_size_log2;
-  const uint32_t row_stride = (uint32_t)(hkv * C);         // bytes between tokens
-  const uint8_t* kbase = a.key_cache + (size_t)h * C;
-  const uint8_t* vbase = a.value_cache + (size_t)h * C;
-  constexpr int stride = 32 * NWH;
-
-  constexpr int WAVE_BYTES = NS * R::SLOT;                 // NS slots per wave
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][WAVE_BYTES];
-  uint8_t* myring = ring[wave_all];
-
-  // start streaming this wave's first NS tiles before the set-up work
-  const int k_first = kbeg + 32 * wave;
-  if (kbeg < kend) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      issue_tile<KVF, D>(myring + j * R::SLOT, k_first + j * stride, kend, lbs,
-                         tile_offsets(k_first + j * stride, kend, lbs, table, row_stride), kbase,
-                         vbase, row_stride, lane);
-  }
-
-  f16x8 qhi[NQK], qlo[NQK];
-  float Mh;
-  fold_query<D, KVF, SM, TQ>(a, h, q0, G, col, grp, qhi, qlo, Mh);
-  const float c2 = a.softmax_scale * Mh * kLog2e;          // score -> log2 units
-
-  // ---- per-wave online softmax over this wave's tiles ----
-  WaveState<D> st;
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  if (kbeg < kend) {
-    int cur = 0;
-    // block offsets of the tile issued next, fetched one iteration early
-    TileOffsets nxt = tile_offsets(k_first + NS * stride, kend, lbs, table, row_stride);
-    for (int k = k_first; k < kend; k += stride) {
-      // this tile's copies are done once at most the later tiles' remain
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt_le<(NS - 1) * 2 * R::NI>();
-      __builtin_amdgcn_sched_barrier(0);
-      uint8_t* slot = myring + cur * R::SLOT;
-      TileRaw<KVF, D> t;
-      read_tile<KVF, D>(slot, t, col, grp);
-      // the slot is refilled (NS tiles ahead) once every lane has read it
-      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
-      __builtin_amdgcn_sched_barrier(0);
-      issue_tile<KVF, D>(slot, k + NS * stride, kend, lbs, nxt, kbase, vbase, row_stride, lane);
-      nxt = tile_offsets(k + (NS + 1) * stride, kend, lbs, table, row_stride);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile<KVF, D>(t, k, kend, c2, qhi, qlo, st, grp);
-      cur = (cur + 1 == NS) ? 0 : cur + 1;
-    }
-  }
-  // drain this wave's outstanding copies before its ring is reused below
-  wait_vmcnt_le<0>();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
-  const float l_run = rows_sum(st.l);
-  __shared__ float sm_ml[NW][2][kDecMaxGroup];             // running max, sum per wave
-  float* wo = reinterpret_cast<float*>(myring);             // [kDecMaxGroup][D] per wave
-  static_assert(kDecMaxGroup * D * 4 <= WAVE_BYTES, "merge area");
-  if (col < G) {
-    if (grp == 0) { sm_ml[wave_all][0][col] = st.m; sm_ml[wave_all][1][col] = l_run; }
-#pragma unroll
-    for (int nbk = 0; nbk < NPV; ++nbk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wo[col * D + (D / 16) * (4 * grp + r) + nbk] = st.o[nbk][r];
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < HP * G * D; t += NW * 64) {
-    const int hs = t / (G * D), cq = (t / D) % G, d = t % D;
-    const int w0 = hs * NWH;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NWH; ++w) M = fmaxf(M, sm_ml[w0 + w][0][cq]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NWH; ++w) {
-        const float f = fast_exp2(sm_ml[w0 + w][0][cq] - M);
-        L += f * sm_ml[w0 + w][1][cq];
-        O += f * reinterpret_cast<const float*>(ring[w0 + w])[cq * D + d];
-      }
-    }
-    const int ho = blockIdx.x * HP + hs;
-    const int hq = ho * G + cq;
-    const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
-    const float val = (L > 0.f) ? O / L * vs : 0.f;          // both carry 2^7
-    reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split-KV decode.  One workgroup per (sequence, group of HG adjacent kv heads,
-// run of consecutive chunks), one wave per head; the host sizes the runs so
-// that the grid is resident at once.  The HG heads' slices of a cache row are
-// adjacent in memory, so the workgroup copies whole HG*C-byte row segments
-// HBM -> LDS: every global_load_lds_dwordx4 moves 1 KB of consecutive bytes,
-// and the waves share the copies of a tile equally.  The ring of NS tile slots
-// belongs to the workgroup and runs on across chunk ends; one barrier per tile
-// both publishes the tile whose copies each wave has waited for and frees the
-// slot read in the step before.  At the end of each chunk every wave writes
-// the partial output (not yet multiplied by the value scale, which the combine
-// applies once) and log-sum-exp of its G query heads.
-// ---------------------------------------------------------------------------
-template <int KVF, int D, int HG> struct SplitGeo {
-  static constexpr int C = KvGeom<KVF, D>::C;
-  static constexpr int RB = HG * C;                          // bytes of a row segment
-  static constexpr int RB16 = RB / 16;                       // its 16-byte chunks
-  static constexpr int SWM = (RB16 < 16 ? RB16 : 16) - 1;   // chunk swizzle mask
-  static constexpr int TILE = 64 * RB;                       // 32 K rows + 32 V rows
-  static constexpr int NIW = C / 16;                         // 1 KB copies per wave per tile
-  static constexpr int ROWS_PER_COPY = 64 / RB16;
-  static_assert(RB16 >= 2 && (RB16 & (RB16 - 1)) == 0, "row segment");
-};
-
-// LDS offset of byte b of row r's segment inside the K (or V) half of a slot:
-// chunk (b / 16) of row r sits at chunk position (b / 16) ^ (r & SWM).
-template <int KVF, int D, int HG>
-__device__ __forceinline__ int split_off(int r, int b) {
-  using SG = SplitGeo<KVF, D, HG>;
-  return r * SG::RB + 16 * ((b >> 4) ^ (r & SG::SWM)) + (b & 15);
-}
-
-// Copy j (0..NIW-1) of this wave fills slot bytes [1024q, 1024q + 1024) with
-// q = j*HG + wave; its lane l loads the chunk that belongs at chunk position
-// 64q + l of the K rows (q < RB16/2) or of the V rows.
-template <int KVF, int D, int HG> struct SplitCopy {
-  using SG = SplitGeo<KVF, D, HG>;
-  int r[SG::NIW];             // tile row of this lane's chunk, per copy
-  uint32_t lane_off[SG::NIW]; // r * row_stride + 16 * global chunk, per copy
-
-  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_stride) {
-#pragma unroll
-    for (int j = 0; j < SG::NIW; ++j) {
-      const int q = j * HG + wave;
-      const int pr = (q % (SG::RB16 / 2)) * 64 + lane;
-      r[j] = pr / SG::RB16;
-      const int gc = (pr % SG::RB16) ^ (r[j] & SG::SWM);
-      lane_off[j] = (uint32_t)r[j] * row_stride + 16u * (uint32_t)gc;
-    }
-  }
-
-  // Queue this wave's copies of the tile at key k0 of a chunk ending at kend.
-  // In a tile cut by the chunk end, rows past it repeat the chunk's last row.
-  __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs, TileOffsets to,
-                                        const uint8_t* kbase, const uint8_t* vbase,
-                                        uint32_t row_stride, int wave) const {
-    const int bmask = (1 << lbs) - 1;
-    const bool full = k0 + 32 <= kend;
-    // k0 is a multiple of 16: key k0 + r sits in row (k0 & bmask) + r of the
-    // block at to.off0 for r < 16, and in row ((k0 + 16) & bmask) + r - 16 of
-    // the block at to.off1 otherwise (the same block when block_size >= 32)
-    const size_t base0 = to.off0 + (size_t)((uint32_t)(k0 & bmask) * row_stride);
-    const size_t base1 = to.off1 + (size_t)((uint32_t)((k0 + 16) & bmask) * row_stride) -
-                         (size_t)(16u * row_stride);
-#pragma unroll
-    for (int j = 0; j < SG::NIW; ++j) {
-      const int q = j * HG + wave;                         // wave-uniform
-      const bool is_v = q >= SG::RB16 / 2;
-      const uint8_t* base = is_v ? vbase : kbase;
-      size_t off;
-      if (full) {
-        off = (r[j] < 16 ? base0 : base1) + lane_off[j];
-      } else {
-        const int rr = r[j];
-        const uint32_t row = (uint32_t)(min(k0 + rr, kend - 1) & bmask);
-        off = (rr < 16 ? to.off0 : to.off1) + row * row_stride +
-              (lane_off[j] - (uint32_t)rr * row_stride);
-      }
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(base + off),
-          (__attribute__((address_space(3))) void*)(slot + q * 1024), 16, 0, kNonTemporal);
-    }
-  }
-};
-
-// This wave's (head `wave` of the group) operand bytes of one tile.
-template <int KVF, int D, int HG>
-__device__ __forceinline__ void read_split_tile(const uint8_t* slot, TileRaw<KVF, D>& t,
-                                                int col, int grp, int wave) {
-  using Geo = KvGeom<KVF, D>;
-  using SG = SplitGeo<KVF, D, HG>;
-  constexpr int KB = Geo::KBYTES, C = Geo::C;
-  const int hb = wave * C;                                 // head's first byte in the segment
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = 16 * hh + col;
-    if constexpr (KB >= 16) {
-#pragma unroll
-      for (int j = 0; j < KB / 16; ++j)
-        lds_bytes<16>(slot + split_off<KVF, D, HG>(r, hb + KB * grp + 16 * j), &t.kw[hh][4 * j]);
-    } else {
-      lds_bytes<KB>(slot + split_off<KVF, D, HG>(r, hb + KB * grp), t.kw[hh]);
-    }
-  }
-  const uint8_t* vs = slot + 32 * SG::RB;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int r = e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
-    t.vw[e][1] = 0;
-    lds_bytes<Geo::VBYTES>(vs + split_off<KVF, D, HG>(r, hb + Geo::VBYTES * col), t.vw[e]);
-  }
-}
-
 // Key range of chunk c: blocks [c*nb/S, (c+1)*nb/S) of the sequence.
 // (c * nb stays below 2^32: the host bounds max_blocks_per_seq * num_splits.)
 __device__ __forceinline__ void chunk_keys(int c, int nb, int S, int bs, int kv_len, int& kb,
@@ -663,126 +458,168 @@ __device__ __forceinline__ void chunk_keys(int c, int nb, int S, int bs, int kv_
   ke = min(kv_len, (int)(((uint32_t)(c + 1) * (uint32_t)nb) / (uint32_t)S) * bs);
 }
 
-// Position of the next tile to copy: chunk pc, key pk (< pke), or pc == c1.
-struct TileCursor {
-  int pc, pk, pke;
-  __device__ __forceinline__ void settle(int c1, int nb, int S, int bs, int kv_len) {
-    while (pc < c1 && pk >= pke) {
-      if (++pc < c1) chunk_keys(pc, nb, S, bs, kv_len, pk, pke);
-    }
-  }
-};
-
-template <int D, int KVF, int SM, typename TQ, int HG, int NS>
-__global__ __launch_bounds__(HG * 64) void decode_split_kernel(
+// Decode over one group of HW adjacent kv heads (blockIdx.x) of sequence
+// blockIdx.y.
+//  * Single pass (SPLIT false): the NW waves of the workgroup take the 32-key
+//    tiles of the whole sequence in turn, each with its own online softmax,
+//    and merge through LDS at the end.
+//  * Split-KV (SPLIT true): wave w of workgroup z takes chunk z * NW + w
+//    (blocks [c*nb/S, (c+1)*nb/S), "GQA GEMV decode", section 2) and writes the
+//    chunk's partial output -- normalised, value scale not yet applied; the
+//    combine applies it once -- and its log-sum-exp.  The waves never
+//    synchronise.
+template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
   using Geo = KvGeom<KVF, D>;
-  using SG = SplitGeo<KVF, D, HG>;
-  static_assert(NS == 2 || NS == 3, "ring depth");
-  constexpr int C = Geo::C, NQK = Geo::NQK, NPV = Geo::NPV;
+  using SG = StreamGeo<KVF, D, HW>;
+  constexpr int NQK = Geo::NQK, NPV = Geo::NPV;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = blockIdx.x * HG + wave, b = blockIdx.y;
+  const int b = blockIdx.y;
   const int q0 = a.cum_q[b];
-  if (a.cum_q[b + 1] == q0) return;                         // no new token: no rows
+  if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
   const int kv_len = a.past_lens[b] + 1;
-  const int bs = a.block_size, hkv = a.hkv, H = a.num_heads;
+  const int hkv = a.hkv, H = a.num_heads;
   const int G = H / hkv;
-  const int nb = (kv_len + bs - 1) / bs;
-  const int S = a.num_splits;
-  const int c0 = blockIdx.z * a.split_chunks_per_wg;
-  const int c1 = min(S, c0 + a.split_chunks_per_wg);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
   const int lbs = a.block_size_log2;
-  const uint32_t row_stride = (uint32_t)(hkv * C);
+  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+  const uint32_t row_stride = (uint32_t)(hkv * Geo::C);   // bytes between tokens
   const uint8_t* kbase = a.key_cache + (size_t)blockIdx.x * SG::RB;
   const uint8_t* vbase = a.value_cache + (size_t)blockIdx.x * SG::RB;
 
-  // query and key-scale loads go out before the tile copies
-  QueryRaw<D, SM> qraw;
-  load_query<D, SM, TQ>(a, h, q0, G, col, grp, qraw);
-  __builtin_amdgcn_sched_barrier(0);
-
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SG::TILE];
-  SplitCopy<KVF, D, HG> cp;
-  cp.init(wave, lane, row_stride);
-  TileCursor pcur;
-  pcur.pc = c0;
-  chunk_keys(c0, nb, S, bs, kv_len, pcur.pk, pcur.pke);
-  pcur.settle(c1, nb, S, bs, kv_len);
-  int issued = 0;
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j) {
-    if (pcur.pc < c1) {
-      cp.issue(ring + j * SG::TILE, pcur.pk, pcur.pke, lbs,
-               tile_offsets(pcur.pk, pcur.pke, lbs, table, row_stride), kbase, vbase, row_stride,
-               wave);
-      ++issued;
-      pcur.pk += 32;
-      pcur.settle(c1, nb, S, bs, kv_len);
-    }
+  // this wave's key range [kb, ke) and its tile stride
+  int kb, ke, stride, chunk = 0;
+  if constexpr (SPLIT) {
+    chunk = blockIdx.z * NW + wave;
+    if (chunk >= a.num_splits) return;                    // no workgroup barrier in split mode
+    const int nb = (kv_len + a.block_size - 1) >> lbs;
+    chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
+    stride = 32;
+  } else {
+    kb = 32 * wave;
+    ke = kv_len;
+    stride = 32 * NW;
   }
-  TileOffsets nxt = tile_offsets(pcur.pc < c1 ? pcur.pk : 0, pcur.pc < c1 ? pcur.pke : 1, lbs,
-                                 table, row_stride);
-  __builtin_amdgcn_sched_barrier(0);
 
-  f16x8 qhi[NQK], qlo[NQK];
-  float Mh;
-  fold_loaded_query<D, KVF, SM, TQ>(qraw, qhi, qlo, Mh);
-  const float c2 = a.softmax_scale * Mh * kLog2e;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NS * SG::SLOT];
+  uint8_t* myring = ring[wave];
+  WaveCopy<KVF, D, HW> cp;
+  cp.init(lane, row_stride);
 
-  int consumed = 0, cur = 0;
-  for (int c = c0; c < c1; ++c) {
-    int kb, ke;
-    chunk_keys(c, nb, S, bs, kv_len, kb, ke);
-    WaveState<D> st;
+  // query and key-scale loads go out first, then this wave's first NS tiles
+  QueryRaw<D, SM> qraw[HW];
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) st.o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int k = kb; k < ke; k += 32) {
-      // this wave's copies of the tile are done (those of the next may fly)
-      __builtin_amdgcn_sched_barrier(0);
-      if (NS == 3 && issued - consumed > 1) wait_vmcnt_le<SG::NIW>();
-      else wait_vmcnt_le<0>();
-      // every wave's copies of the tile are done, and every wave has read the
-      // slot about to be refilled
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (pcur.pc < c1) {
-        cp.issue(ring + ((cur + NS - 1) % NS) * SG::TILE, pcur.pk, pcur.pke, lbs, nxt, kbase,
-                 vbase, row_stride, wave);
-        ++issued;
-        pcur.pk += 32;
-        pcur.settle(c1, nb, S, bs, kv_len);
-        if (pcur.pc < c1) nxt = tile_offsets(pcur.pk, pcur.pke, lbs, table, row_stride);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      TileRaw<KVF, D> tr;
-      read_split_tile<KVF, D, HG>(ring + cur * SG::TILE, tr, col, grp, wave);
-      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): slot reads done
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile<KVF, D>(tr, k, ke, c2, qhi, qlo, st, grp);
-      ++consumed;
-      cur = (cur + 1 == NS) ? 0 : cur + 1;
-    }
-    // partial output (value scale not applied) and log-sum-exp of chunk c
-    const float L = rows_sum(st.l);
-    if (col < G) {
-      const int hq = h * G + col;
-      const size_t pi = ((size_t)q0 * H + hq) * S + c;
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;          // both carry 2^7
-      float* po = a.part_o + pi * D;
+  for (int hh = 0; hh < HW; ++hh)
+    load_query<D, SM, TQ>(a, blockIdx.x * HW + hh, q0, G, col, grp, qraw[hh]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = (D / 16) * (4 * grp + r);
+  for (int j = 0; j < NS; ++j)
+    if (kb + j * stride < ke)
+      cp.issue(myring + j * SG::SLOT, kb + j * stride, ke, lbs, table, kbase, vbase, row_stride);
+  // The waits below count NS - 1 tiles in flight behind the current one; with
+  // fewer tiles than that, wait for everything instead.
+  if (kb + (NS - 1) * stride >= ke) wait_vmcnt_le<0>();
+
+  f16x8 qhi[HW][NQK], qlo[HW][NQK];
+  float c2[HW];
 #pragma unroll
-        for (int nbk = 0; nbk < NPV; ++nbk) po[d0 + nbk] = st.o[nbk][r] * inv;
-      }
-      if (grp == 0)
-        a.part_lse[pi] = (L > 0.f) ? (st.m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
-    }
+  for (int hh = 0; hh < HW; ++hh) {
+    float Mh;
+    fold_loaded_query<D, KVF, SM, TQ>(qraw[hh], qhi[hh], qlo[hh], Mh);
+    c2[hh] = a.softmax_scale * Mh * kLog2e;               // score -> log2 units
+  }
+
+  WaveState<D> st[HW];
+#pragma unroll
+  for (int hh = 0; hh < HW; ++hh)
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) st[hh].o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int cur = 0;
+  for (int k = kb; k < ke; k += stride) {
+    // this tile's copies are done once at most the later tiles' remain
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_le<(NS - 1) * 2 * SG::NI>();
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* slot = myring + cur * SG::SLOT;
+    TileRaw<KVF, D> t[HW];
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) read_tile<KVF, D, HW>(slot, t[hh], col, grp, hh);
+    // the slot is refilled (NS tiles ahead) once every lane has read it
+    __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    const int kn = k + NS * stride;
+    if (kn < ke) cp.issue(slot, kn, ke, lbs, table, kbase, vbase, row_stride);
+    else wait_vmcnt_le<0>();                              // nothing more to issue: keep vmcnt exact
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh)
+      compute_tile<KVF, D>(t[hh], k, ke, c2[hh], qhi[hh], qlo[hh], st[hh], grp);
+    cur = (cur + 1 == NS) ? 0 : cur + 1;
   }
   wait_vmcnt_le<0>();
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (SPLIT) {
+    // partial output (value scale not applied) and log-sum-exp of the chunk
+    const int S = a.num_splits;
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const float L = rows_sum(st[hh].l);
+      if (col < G) {
+        const int hq = (blockIdx.x * HW + hh) * G + col;
+        const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
+        const float inv = (L > 0.f) ? 1.f / L : 0.f;      // both carry 2^7
+        float* po = a.part_o + pi * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d0 = (D / 16) * (4 * grp + r);
+#pragma unroll
+          for (int nbk = 0; nbk < NPV; ++nbk) po[d0 + nbk] = st[hh].o[nbk][r] * inv;
+        }
+        if (grp == 0)
+          a.part_lse[pi] = (L > 0.f) ? (st[hh].m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
+      }
+    }
+  } else {
+    // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
+    __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];      // running max, sum per wave
+    float* wo = reinterpret_cast<float*>(myring);          // [HW][kDecMaxGroup][D] per wave
+    static_assert(HW * kDecMaxGroup * D * 4 <= NS * SG::SLOT, "merge area");
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const float l_run = rows_sum(st[hh].l);
+      if (col < G) {
+        if (grp == 0) { sm_ml[wave][hh][0][col] = st[hh].m; sm_ml[wave][hh][1][col] = l_run; }
+#pragma unroll
+        for (int nbk = 0; nbk < NPV; ++nbk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            wo[(hh * kDecMaxGroup + col) * D + (D / 16) * (4 * grp + r) + nbk] = st[hh].o[nbk][r];
+      }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < HW * G * D; t += NW * 64) {
+      const int hh = t / (G * D), cq = (t / D) % G, d = t % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][hh][0][cq]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = fast_exp2(sm_ml[w][hh][0][cq] - M);
+          L += f * sm_ml[w][hh][1][cq];
+          O += f * reinterpret_cast<const float*>(ring[w])[(hh * kDecMaxGroup + cq) * D + d];
+        }
+      }
+      const int ho = blockIdx.x * HW + hh;
+      const int hq = ho * G + cq;
+      const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
+      const float val = (L > 0.f) ? O / L * vs : 0.f;        // both carry 2^7
+      reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
+    }
+  }
 }
 
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype) {
@@ -790,75 +627,58 @@ bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype)
          block_size >= 16 && block_size % 16 == 0 && (q_dtype == DT_F16 || q_dtype == DT_BF16);
 }
 
-template <int D, int KVF, int SM, int NW, int NS, int HP>
-static int launch_dqw(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.hkv / HP, a.batch, 1);
-  if (a.q_dtype == DT_F16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, f16, NW, NS, HP>), grid, dim3(NW * 64), 0,
-                       st, a, a.block_table);
-  else if (a.q_dtype == DT_BF16)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KVF, SM, bf16, NW, NS, HP>), grid, dim3(NW * 64), 0,
-                       st, a, a.block_table);
-  else
-    return -1;
+// Launch with HW heads per wave.  Single pass: grid (hkv / HW, batch), 8 waves
+// per (sequence, head group), NS = 1 tile in flight per wave besides the one
+// being read (the copies of 8 waves then keep ~64 KB per CU in flight, where
+// measured HBM efficiency peaks).  Split-KV: grid (hkv / HW, batch,
+// ceil(S / NW)), one wave per chunk, NS = 2; NW = 8 waves per workgroup when
+// that still gives every compute unit a workgroup, else 4.
+template <int D, int KVF, int SM, typename TQ, int HW, int NW>
+static void launch_split_nw(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.hkv / HW, a.batch, (a.num_splits + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, NW, 2, HW, true>), grid,
+                     dim3(NW * 64), 0, st, a, a.block_table);
+}
+
+template <int D, int KVF, int SM, typename TQ, int HW>
+static int launch_hw_q(const AttnArgs& a, hipStream_t st) {
+  if (a.num_splits > 1) {
+    const long waves = (long)(a.hkv / HW) * a.batch * a.num_splits;
+    if (waves >= 8L * (a.num_cus > 0 ? a.num_cus : 256))
+      launch_split_nw<D, KVF, SM, TQ, HW, 8>(a, st);
+    else
+      launch_split_nw<D, KVF, SM, TQ, HW, 4>(a, st);
+  } else {
+    dim3 grid(a.hkv / HW, a.batch, 1);
+    hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, 8, 1, HW, false>), grid,
+                       dim3(8 * 64), 0, st, a, a.block_table);
+  }
   return 0;
 }
 
-// Split-KV: HG = the largest of 8, 4, 2, 1 that divides the kv head count.
-// Each workgroup takes a run of consecutive chunks, sized so that the whole
-// grid is resident at once.
-template <typename K>
-static int resident_wgs_per_cu(K kernel, int threads) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
-    n = 1;
-  return n;
-}
-
-template <int D, int KVF, int SM, typename TQ, int HG>
-static int launch_split_hg_q(const AttnArgs& a0, hipStream_t st) {
-  constexpr int NS = (3 * SplitGeo<KVF, D, HG>::TILE <= 160 * 1024) ? 3 : 2;
-  auto kernel = decode_split_kernel<D, KVF, SM, TQ, HG, NS>;
-  static int per_cu = 0;                                  // kernel property: same on every call
-  if (per_cu == 0) per_cu = resident_wgs_per_cu(kernel, HG * 64);
-  AttnArgs a = a0;
-  const long units = (long)(a.hkv / HG) * a.batch * a.num_splits;
-  const long slots = (long)(a.num_cus > 0 ? a.num_cus : 256) * per_cu;
-  a.split_chunks_per_wg = (int)((units + slots - 1) / slots);
-  const int runs = (a.num_splits + a.split_chunks_per_wg - 1) / a.split_chunks_per_wg;
-  dim3 grid(a.hkv / HG, a.batch, runs);
-  hipLaunchKernelGGL(kernel, grid, dim3(HG * 64), 0, st, a, a.block_table);
-  return 0;
-}
-
-template <int D, int KVF, int SM, int HG>
-static int launch_split_hg(const AttnArgs& a, hipStream_t st) {
-  if (a.q_dtype == DT_F16) return launch_split_hg_q<D, KVF, SM, f16, HG>(a, st);
-  if (a.q_dtype == DT_BF16) return launch_split_hg_q<D, KVF, SM, bf16, HG>(a, st);
+template <int D, int KVF, int SM, int HW>
+static int launch_hw(const AttnArgs& a, hipStream_t st) {
+  if (a.q_dtype == DT_F16) return launch_hw_q<D, KVF, SM, f16, HW>(a, st);
+  if (a.q_dtype == DT_BF16) return launch_hw_q<D, KVF, SM, bf16, HW>(a, st);
   return -1;
 }
 
-template <int D, int KVF, int SM>
-static int launch_split(const AttnArgs& a, hipStream_t st) {
-  if (a.hkv % 8 == 0) return launch_split_hg<D, KVF, SM, 8>(a, st);
-  if (a.hkv % 4 == 0) return launch_split_hg<D, KVF, SM, 4>(a, st);
-  if (a.hkv % 2 == 0) return launch_split_hg<D, KVF, SM, 2>(a, st);
-  return launch_split_hg<D, KVF, SM, 1>(a, st);
-}
-
-// Single pass: one workgroup per (sequence, kv head) whose waves take the
-// tiles in turn and merge at the end; rows shorter than a 128-byte line
-// (packed INT4 with D=128, any format with D=64) pair two kv heads per
-// workgroup so both halves of every line are read by the same CU.  Split-KV:
-// one wave per kv head of a group of HG adjacent heads, per run of chunks.
+// HW = 128 / C heads per wave when the kv head count allows (whole 128-byte
+// lines per copied row segment), else the largest power of two dividing it.
 template <int D, int KVF, int SM>
 static int launch_dq(const AttnArgs& a, hipStream_t st) {
-  if (a.num_splits > 1) return launch_split<D, KVF, SM>(a, st);
-  constexpr bool short_rows = KvGeom<KVF, D>::C < 128;
-  if constexpr (short_rows) {
-    if (a.hkv % 2 == 0) return launch_dqw<D, KVF, SM, 8, 2, 2>(a, st);
+  constexpr int C = KvGeom<KVF, D>::C;
+  if constexpr (C >= 128) {
+    return launch_hw<D, KVF, SM, 1>(a, st);
+  } else if constexpr (C == 64) {
+    if (a.hkv % 2 == 0) return launch_hw<D, KVF, SM, 2>(a, st);
+    return launch_hw<D, KVF, SM, 1>(a, st);
+  } else {
+    static_assert(C == 32, "row bytes");
+    if (a.hkv % 4 == 0) return launch_hw<D, KVF, SM, 4>(a, st);
+    if (a.hkv % 2 == 0) return launch_hw<D, KVF, SM, 2>(a, st);
+    return launch_hw<D, KVF, SM, 1>(a, st);
   }
-  return launch_dqw<D, KVF, SM, 8, 1, 1>(a, st);
 }
 
 template <int D>
