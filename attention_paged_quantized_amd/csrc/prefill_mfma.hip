@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     for (int i = 0; i < Geo::VU_PER_T; ++i) {
       const int u = tid + i * kPfThreads;
       if (Geo::VUNITS % kPfThreads && u >= Geo::VUNITS) break;
-      const int m = u / Geo::UPR, c = u % Geo::UPR;
+      const int m = u % (kBN / 2), c = u / (kBN / 2);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         rs.va[i][e] = vbase + row_off(tb, kt, 2 * m + e) + 16 * c;
@@ -284,7 +284,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     for (int i = 0; i < Geo::VU_PER_T; ++i) {
       const int u = tid + i * kPfThreads;
       if (Geo::VUNITS % kPfThreads && u >= Geo::VUNITS) break;
-      const int m = u / Geo::UPR, c = u % Geo::UPR;
+      // consecutive lanes take consecutive key pairs of one 16-byte unit: the
+      // 32 lanes of a write then hit 32 different V^T-row banks
+      const int m = u % (kBN / 2), c = u / (kBN / 2);
       uint32_t w0[Geo::CPU / 2], w1[Geo::CPU / 2];
       decode_unit<KVF, f16>(rs.v[i][0], w0);
       decode_unit<KVF, f16>(rs.v[i][1], w1);
@@ -403,11 +405,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[st][r], c2, bias));
-          l_run += pv;
-          p[2 * st + (r >> 3)][r & 7] = (f16)pv;
-        }
+        for (int r = 0; r < 16; ++r)
+          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
+      // the running sum adds the fp16 values the PV product uses, two per dot
+      const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
+      float lp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lp[i] = __builtin_amdgcn_fdot2((f16x2){p[c][2 * i], p[c][2 * i + 1]}, ones, lp[i],
+                                         false);
+      l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
       // O^T += V^T P^T, with the V^T operands of the next channel tile read
       // while the current tile's MFMAs run
       {
