@@ -12,10 +12,15 @@
 //
 // Per 64-key KV tile ("FlashInfer FP8 KV-cache prefill", repack section: convert
 // once into shared memory instead of per use):
-//   * all 256 threads load the codes of the next tile while the current one is
-//     computed, then convert them exactly to 16-bit values in LDS (double
-//     buffered): K row-major, V transposed (channel-major) with keys in the order
-//     the PV operand wants; rows are padded by 16 bytes against bank conflicts;
+//   * all 256 threads load the codes of tile kt+2 while tile kt is computed,
+//     and convert the codes of tile kt+1 exactly to 16-bit values in the other
+//     LDS buffer beside tile kt's products (K rows beside the QK MFMAs, V^T rows
+//     beside the PV MFMAs), so the conversion's VALU and LDS work overlaps the
+//     matrix cores: K row-major, V transposed (channel-major) with keys in the
+//     order the PV operand wants; rows are padded by 16 bytes against bank
+//     conflicts;
+//   * two 4-wave workgroups share a compute unit, so each SIMD interleaves
+//     waves of two independent workgroups;
 //   * S^T = K Q'^T: A = 32 keys x 16 channels of K, B = Q'^T (lane: query column
 //     l%32), so every lane owns one query column and reduces its softmax row
 //     with a single cross-lane exchange (lanes l and l^32);
@@ -24,7 +29,7 @@
 //   * O^T += V^T P^T with fp16 P scaled by 2^7 under a lazily refreshed running
 //     maximum (rescale only when a score exceeds it by more than 2^8);
 //   * causal mask (row i sees keys <= past + i) only where a tile crosses the
-//     diagonal; a wave skips the math of tiles entirely above its rows.
+//     diagonal.
 // Key scales: per-channel scales are folded into the query (power-of-two
 // normaliser M_h >= max|s|, "ONNX Runtime: INT4 Paged KV Cache", section 3);
 // per-head scales go into the score factor.  Value scales are applied in the
@@ -38,7 +43,7 @@ namespace paq {
 namespace {
 
 constexpr int kBN = 64;                      // keys per KV tile
-constexpr int kPfWavesPerGroup = 8;          // waves per workgroup (32/G tokens each)
+constexpr int kPfWavesPerGroup = 4;          // waves per workgroup (32/G tokens each)
 constexpr float kPfSlack = 8.0f;             // lazy running-max slack (log2 units)
 constexpr float kPfPScaleLog2 = 7.0f;        // fp16 P = p * 2^7
 
@@ -200,8 +205,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int tok_end = min(qlen, tok0 + TOK);
   const int kv_end = past + tok_end;                          // exclusive
   const int ntiles = (kv_end + kBN - 1) / kBN;
-  const int wtok_last = min(tok_end, tok0 + (wave + 1) * TPW) - 1;
-  const int wave_lim = past + wtok_last;                      // last key any row of the wave sees
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][Geo::TILE];
 
@@ -263,10 +266,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < Geo::VU_PER_T; ++i) asm volatile("" ::"v"(rs.va[i][0]), "v"(rs.va[i][1]));
   };
-  auto store_tile = [&](const RawSet& rs, int buf) {
+  // Convert the codes of a tile into LDS buffer `buf`: K rows (store_k) and
+  // V^T rows (store_v), done beside the QK and the PV products respectively.
+  auto store_k = [&](const RawSet& rs, int buf) {
     keep_addresses(rs);
     uint8_t* kl = lds[buf];
-    uint8_t* vl = lds[buf] + kBN * Geo::KROW;
 #pragma unroll
     for (int i = 0; i < Geo::KU_PER_T; ++i) {
       const int u = tid + i * kPfThreads;
@@ -280,6 +284,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
         *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 2 * Geo::CPU * c + 16 * j) =
             (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
     }
+  };
+  auto store_v = [&](const RawSet& rs, int buf) {
+    keep_addresses(rs);
+    uint8_t* vl = lds[buf] + kBN * Geo::KROW;
 #pragma unroll
     for (int i = 0; i < Geo::VU_PER_T; ++i) {
       const int u = tid + i * kPfThreads;
@@ -303,9 +311,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 
   RawSet ra, rb;
   TileBlocks tb_next = tile_blocks(0);
-  if (ntiles > 0) load_codes(ra, tb_next, 0);
+  load_codes(ra, tb_next, 0);
   tb_next = tile_blocks(1);
-  if (ntiles > 1) load_codes(rb, tb_next, 1);
+  load_codes(rb, tb_next, 1);
   tb_next = tile_blocks(2);
 
   // ---- query operand: Q'^T columns, fold of the key scale ----
@@ -343,71 +351,80 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
 
-  auto compute = [&](int kt) {
+  // One 64-key tile: S^T = K Q'^T for two 32-key blocks, causal mask, lazy
+  // online softmax, O^T += V^T P^T.  The conversion of the next tile (codes in
+  // `nxt`) into the other LDS buffer runs beside the MFMAs: its K rows beside
+  // the QK products, its V^T rows beside the PV products.
+  // (sched_group_barrier masks: 0x002 VALU, 0x008 MFMA, 0x100 LDS read,
+  // 0x200 LDS write)
+  auto compute = [&](int kt, const RawSet& nxt, int nbuf) {
     const int buf = kt & 1;
     const int key0 = kt * kBN;
-    if (key0 <= wave_lim) {
-      const uint8_t* kl = lds[buf];
-      const uint8_t* vl = lds[buf] + kBN * Geo::KROW;
-      // S^T for the two 32-key blocks.  All K operands of a block are read
-      // before its MFMAs, and the second block's reads are issued between the
-      // first block's MFMAs, so no MFMA waits on the LDS read just before it.
-      f32x16 s[2] = {(f32x16){}, (f32x16){}};
-      {
-        const uint8_t* k0p = kl + n * Geo::KROW + 16 * eta;
-        const uint8_t* k1p = k0p + 32 * Geo::KROW;
-        kvec ka[NKK];
-        __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* kl = lds[buf];
+    const uint8_t* vl = lds[buf] + kBN * Geo::KROW;
+    f32x16 s[2] = {(f32x16){}, (f32x16){}};
+    {
+      const uint8_t* k0p = kl + n * Geo::KROW + 16 * eta;
+      const uint8_t* k1p = k0p + 32 * Geo::KROW;
+      kvec ka[NKK];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) ka[kk] = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
+      for (int kk = 0; kk < NKK; ++kk) ka[kk] = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s[0] = MK::run(ka[kk], qop[kk], s[0]);
-          ka[kk] = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s[1] = MK::run(ka[kk], qop[kk], s[1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NKK, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[0] = MK::run(ka[kk], qop[kk], s[0]);
+        ka[kk] = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
       }
-      // causal mask on raw scores, lazy running max in log2 units
-      const bool diag = key0 + kBN - 1 > past + tok0 + wave * TPW;   // may need masking
-      float lm = -INFINITY;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int kk = 0; kk < NKK; ++kk) s[1] = MK::run(ka[kk], qop[kk], s[1]);
+      store_k(nxt, nbuf);
+      __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (diag) {
-            const int key = key0 + 32 * st + 8 * (r >> 2) + 4 * eta + (r & 3);
-            s[st][r] = key <= row_lim ? s[st][r] : -INFINITY;
-          }
-          lm = fmaxf(lm, s[st][r]);
-        }
-      lm *= c2;
-      if (__ballot(lm > m_run + kPfSlack)) {
-        const float m_new = fmaxf(m_run, fmaxf(lm, __shfl_xor(lm, 32, 64)));
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDT; ++i) o[i] *= alpha;
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
-      // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
-      // regs 8c..8c+7); l accumulates the same scaled values
-      const float bias = kPfPScaleLog2 - m_run;
-      f16x8 p[4];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // causal mask on raw scores, lazy running max in log2 units
+    const bool diag = key0 + kBN - 1 > past + tok0 + wave * TPW;   // may need masking
+    float lm = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
-      // the running sum adds the fp16 values the PV product uses, two per dot
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (diag) {
+          const int key = key0 + 32 * st + 8 * (r >> 2) + 4 * eta + (r & 3);
+          s[st][r] = key <= row_lim ? s[st][r] : -INFINITY;
+        }
+        lm = fmaxf(lm, s[st][r]);
+      }
+    lm *= c2;
+    if (__ballot(lm > m_run + kPfSlack)) {
+      const float m_new = fmaxf(m_run, fmaxf(lm, __shfl_xor(lm, 32, 64)));
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[i] *= alpha;
+    }
+    // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
+    // regs 8c..8c+7); l accumulates the same fp16 values, two per dot
+    const float bias = kPfPScaleLog2 - m_run;
+    f16x8 p[4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
+    {
       const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
       float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -417,52 +434,59 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
           lp[i] = __builtin_amdgcn_fdot2((f16x2){p[c][2 * i], p[c][2 * i + 1]}, ones, lp[i],
                                          false);
       l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
-      // O^T += V^T P^T, with the V^T operands of the next channel tile read
-      // while the current tile's MFMAs run
-      {
-        const uint8_t* vp = vl + n * Geo::VROW + 16 * eta;
-        f16x8 va[4];
-        __builtin_amdgcn_sched_barrier(0);
+    }
+    // O^T += V^T P^T, with the V^T operands of the next channel tile read
+    // while the current tile's MFMAs run, beside the next tile's V^T staging
+    {
+      const uint8_t* vp = vl + n * Geo::VROW + 16 * eta;
+      f16x8 va[4];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * c);
+      for (int c = 0; c < 4; ++c) va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * c);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c], p[c], o[dt], 0, 0, 0);
-            if (dt + 1 < NDT)
-              va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * (dt + 1) * Geo::VROW + 32 * c);
-          }
+        for (int c = 0; c < 4; ++c) {
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c], p[c], o[dt], 0, 0, 0);
+          if (dt + 1 < NDT)
+            va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * (dt + 1) * Geo::VROW + 32 * c);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 4 * (NDT - 1); ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
+      store_v(nxt, nbuf);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * (NDT - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // tile kt+1's codes are in registers and tile kt+2's are loading while tile
-  // kt is computed; then tile kt+1 is converted into the other LDS buffer
-  if (ntiles > 0) store_tile(ra, 0);
+  // Tile kt+1's codes are in registers and tile kt+2's are loading while tile
+  // kt is computed; tile kt+1 is converted into the other LDS buffer during
+  // the products of tile kt.  Loads past the last tile re-read its final keys
+  // (addresses are clamped) and their conversion lands in the idle buffer.
+  store_k(ra, 0);
+  store_v(ra, 0);
   __syncthreads();
-  int kt = 0;
-  while (true) {
-    if (kt >= ntiles) break;
-    if (kt + 2 < ntiles) { load_codes(ra, tb_next, kt + 2); tb_next = tile_blocks(kt + 3); }
-    compute(kt);
-    if (kt + 1 < ntiles) store_tile(rb, (kt + 1) & 1);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    load_codes(ra, tb_next, kt + 2);
+    tb_next = tile_blocks(kt + 3);
+    compute(kt, rb, (kt + 1) & 1);
     __syncthreads();
-    ++kt;
-    if (kt >= ntiles) break;
-    if (kt + 2 < ntiles) { load_codes(rb, tb_next, kt + 2); tb_next = tile_blocks(kt + 3); }
-    compute(kt);
-    if (kt + 1 < ntiles) store_tile(ra, (kt + 1) & 1);
+    if (kt + 1 >= ntiles) break;
+    load_codes(rb, tb_next, kt + 3);
+    tb_next = tile_blocks(kt + 4);
+    compute(kt + 1, ra, kt & 1);
     __syncthreads();
-    ++kt;
   }
 
   // ---- epilogue: normalise, value scale, store the rows of this wave ----
