@@ -31,8 +31,8 @@ METRIC = "decode KV-cache GB/s (frac of HBM peak) + tokens/s; prefill MFMA util"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, 256 CU x 4096 flop/clk x 2.4 GHz
 KERNEL_SOURCES = {
-    "decode": ["decode_mfma.hip", "combine.hip", "device.hpp"],
-    "prefill": ["prefill_mfma.hip", "device.hpp"],
+    "decode": ["decode_mfma.hip", "combine.hip", "device.hpp", "launch.hpp"],
+    "prefill": ["prefill_mfma.hip", "device.hpp", "launch.hpp"],
 }
 
 
@@ -141,14 +141,13 @@ def cpu_baseline(w, seconds):
 
 
 # Kernels of one attention call, by workload kind (substrings of the symbol).
-CALL_KERNELS = {"decode": ("decode_mfma_kernel", "decode_split_kernel", "combine_kernel",
-                           "attn_f32_kernel"),
+CALL_KERNELS = {"decode": ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel"),
                 "prefill": ("prefill_mfma_kernel", "attn_f32_kernel")}
 CALIB_KERNEL = "neg_kernel"
 
 
 def _short(name):
-    for k in ("decode_mfma_kernel", "decode_split_kernel", "combine_kernel", "attn_f32_kernel",
+    for k in ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel",
               "prefill_mfma_kernel", "quant_append_kernel", CALIB_KERNEL):
         if k in name:
             return k
@@ -403,7 +402,7 @@ def main():
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                               "kernel": "paged_attn_decode call (%s)" %
-                                        ("decode_mfma" + (" + combine" if S > 1 else "")),
+                                        ("decode_stream_kernel" + (" + combine_kernel" if S > 1 else "")),
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
                               "kernel_us_p10_p90": [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
                                                     round(kern_sorted[9 * len(kern_ms) // 10] * 1e3, 3)],
@@ -418,7 +417,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                               "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                               "traffic": counters(w.name, "prefill", fl),
-                              "kernel": "paged_attn_prefill call (prefill_mfma)",
+                              "kernel": "paged_attn_prefill call (prefill_mfma_kernel)",
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
                               "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
                               "algorithmic_flops_per_launch": fl}
