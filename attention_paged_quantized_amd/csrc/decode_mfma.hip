@@ -76,14 +76,38 @@ __device__ __forceinline__ f16x8 k_operand(const uint32_t* kw, int m) {
     int4x8_to_f16x2x4(kw[m], p);
     r = (f16x8){p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
   } else {
+    // FP8 keys enter as value / 256 (exact); the factor is in the score scale
     const uint32_t w0 = kw[2 * m], w1 = kw[2 * m + 1];
-    f16x2 a = e4m3_hi_bytes_to_f16x2(perm(w0, w0, 0x010C000Cu));
-    f16x2 b = e4m3_hi_bytes_to_f16x2(perm(w0, w0, 0x030C020Cu));
-    f16x2 c = e4m3_hi_bytes_to_f16x2(perm(w1, w1, 0x010C000Cu));
-    f16x2 d = e4m3_hi_bytes_to_f16x2(perm(w1, w1, 0x030C020Cu));
+    f16x2 a = e4m3_hi_bytes_to_f16x2_raw(perm(w0, w0, 0x010C000Cu));
+    f16x2 b = e4m3_hi_bytes_to_f16x2_raw(perm(w0, w0, 0x030C020Cu));
+    f16x2 c = e4m3_hi_bytes_to_f16x2_raw(perm(w1, w1, 0x010C000Cu));
+    f16x2 d = e4m3_hi_bytes_to_f16x2_raw(perm(w1, w1, 0x030C020Cu));
     r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
   return r;
+}
+
+// Scale of the fp16 key operand relative to the key codes (FP8: value / 256).
+template <int KVF> constexpr float kKeyOperandScale = (KVF == KV_FP8) ? 1.f / 256.f : 1.f;
+
+// The V^T operands are affine images of the value codes, v' = a_c + b_c * v:
+//   INT8: 1152 + v (the 0x6400 construction without its bias subtraction);
+//   INT4: 1032 + v for even channels (low nibbles), 1152 + 16 v for odd ones;
+//   FP8:  v / 256.
+// Since the fp16 probabilities P that multiply them sum to l exactly as
+// accumulated (l is the sum of those same fp16 values), the output
+// O = sum_j P_j v_j is recovered from O' = sum_j P_j v'_j as
+// (O'/l - a_c) / b_c.  This saves the per-value bias arithmetic; the
+// subtraction costs ~10 of fp32's 24 bits, far inside the output tolerance.
+template <int KVF>
+__device__ __forceinline__ float v_unbias(float o_over_l, int d) {
+  if constexpr (KVF == KV_INT8) {
+    return o_over_l - 1152.f;
+  } else if constexpr (KVF == KV_INT4) {
+    return (d & 1) ? (o_over_l - 1152.f) * 0.0625f : o_over_l - 1032.f;
+  } else {
+    return o_over_l * 256.f;
+  }
 }
 
 // V^T operands for all NPV MFMAs from the lane's 8 keys (slot e = key e).
@@ -104,16 +128,16 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vw)[8][2], f16x8 (&v
           const uint32_t sel = (uint32_t)sh | ((4u + sh) << 8) | ((uint32_t)(sh + 1) << 16) |
                                ((5u + sh) << 24);
           const uint32_t x = perm(hi, lo, sel) ^ 0x80808080u;
-          const f16x2 p0 = i8pair_to_f16x2(x, 0x04010400u);
-          const f16x2 p1 = i8pair_to_f16x2(x, 0x04030402u);
+          const f16x2 p0 = bitcast<f16x2>(perm(0x64646464u, x, 0x04010400u));   // 1152 + v
+          const f16x2 p1 = bitcast<f16x2>(perm(0x64646464u, x, 0x04030402u));
           vop[nb][e] = p0[0]; vop[nb][e + 1] = p0[1];
           vop[nb + 1][e] = p1[0]; vop[nb + 1][e + 1] = p1[1];
         } else {
           // [0, e.nb, 0, e+1.nb] and the same for nb+1
           const uint32_t s0 = 0x0Cu | ((uint32_t)sh << 8) | (0x0Cu << 16) | ((4u + sh) << 24);
           const uint32_t s1 = 0x0Cu | ((uint32_t)(sh + 1) << 8) | (0x0Cu << 16) | ((5u + sh) << 24);
-          const f16x2 p0 = e4m3_hi_bytes_to_f16x2(perm(hi, lo, s0));
-          const f16x2 p1 = e4m3_hi_bytes_to_f16x2(perm(hi, lo, s1));
+          const f16x2 p0 = e4m3_hi_bytes_to_f16x2_raw(perm(hi, lo, s0));      // v / 256
+          const f16x2 p1 = e4m3_hi_bytes_to_f16x2_raw(perm(hi, lo, s1));
           vop[nb][e] = p0[0]; vop[nb][e + 1] = p0[1];
           vop[nb + 1][e] = p1[0]; vop[nb + 1][e + 1] = p1[1];
         }
@@ -125,7 +149,7 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vw)[8][2], f16x8 (&v
         const uint32_t sel = (uint32_t)j | ((uint32_t)(j + 1) << 8) | ((uint32_t)(4 + j) << 16) |
                              ((uint32_t)(5 + j) << 24);
         f16x2 c[4];
-        int4x8_to_f16x2x4(perm(vw[e + 1][0], vw[e][0], sel), c);
+        int4x8_to_f16x2x4_raw(perm(vw[e + 1][0], vw[e][0], sel), c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           vop[2 * j + i][e] = c[i][0];
@@ -341,17 +365,18 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
 #pragma unroll
     for (int i = 0; i < NPV; ++i) st.o[i] *= alpha;
   }
-  // P' = 2^7 * 2^(s*c2 - m); the running sum carries the same factor
+  // P' = 2^7 * 2^(s*c2 - m) in fp16; the running sum adds exactly those fp16
+  // values (two per dot), which the value unbiasing in the epilogue relies on
   const float bias = kPScaleLog2 - st.m;
   f16x8 pop;
-  float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = fast_exp2(fmaf(v[i], c2, bias));
-    psum += p;
-    pop[i] = (f16)p;
-  }
-  st.l += psum;
+  for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(fmaf(v[i], c2, bias));
+  const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
+  float l0 = __builtin_amdgcn_fdot2((f16x2){pop[0], pop[1]}, ones, st.l, false);
+  float l1 = __builtin_amdgcn_fdot2((f16x2){pop[2], pop[3]}, ones, 0.f, false);
+  l0 = __builtin_amdgcn_fdot2((f16x2){pop[4], pop[5]}, ones, l0, false);
+  l1 = __builtin_amdgcn_fdot2((f16x2){pop[6], pop[7]}, ones, l1, false);
+  st.l = l0 + l1;
   // O^T += V^T P^T
   f16x8 vop[NPV];
   v_operands<KVF, D>(t.vw, vop);
@@ -527,7 +552,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
   for (int hh = 0; hh < HW; ++hh) {
     float Mh;
     fold_loaded_query<D, KVF, SM, TQ>(qraw[hh], qhi[hh], qlo[hh], Mh);
-    c2[hh] = a.softmax_scale * Mh * kLog2e;               // score -> log2 units
+    c2[hh] = a.softmax_scale * Mh * kLog2e / kKeyOperandScale<KVF>;   // score -> log2 units
   }
 
   WaveState<D> st[HW];
@@ -575,7 +600,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
         for (int r = 0; r < 4; ++r) {
           const int d0 = (D / 16) * (4 * grp + r);
 #pragma unroll
-          for (int nbk = 0; nbk < NPV; ++nbk) po[d0 + nbk] = st[hh].o[nbk][r] * inv;
+          for (int nbk = 0; nbk < NPV; ++nbk)
+            po[d0 + nbk] = (L > 0.f) ? v_unbias<KVF>(st[hh].o[nbk][r] * inv, d0 + nbk) : 0.f;
         }
         if (grp == 0)
           a.part_lse[pi] = (L > 0.f) ? (st[hh].m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
@@ -616,7 +642,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
       const int ho = blockIdx.x * HW + hh;
       const int hq = ho * G + cq;
       const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
-      const float val = (L > 0.f) ? O / L * vs : 0.f;        // both carry 2^7
+      const float val = (L > 0.f) ? v_unbias<KVF>(O / L, d) * vs : 0.f;   // both carry 2^7
       reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
     }
   }

@@ -125,6 +125,24 @@ __device__ __forceinline__ void int4x8_to_f16x2x4(uint32_t w, f16x2 (&o)[4]) {
   o[3] = __builtin_elementwise_fma(bitcast<f16x2>(p3), hi_scale, hi_bias);
 }
 
+// The same eight codes as affine fp16 images without the final fixups:
+// o[0], o[2] = 1032 + code (nibbles 0, 2, 4, 6), o[1], o[3] = 1152 + 16 code
+// (nibbles 1, 3, 5, 7); one v_bitop3 per pair.
+__device__ __forceinline__ void int4x8_to_f16x2x4_raw(uint32_t w, f16x2 (&o)[4]) {
+  constexpr uint32_t kMaskedXor = 0x6A;
+  const uint32_t w8 = w >> 8;
+  o[0] = bitcast<f16x2>(__builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, kMaskedXor));
+  o[1] = bitcast<f16x2>(__builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, kMaskedXor));
+  o[2] = bitcast<f16x2>(__builtin_amdgcn_bitop3_b32(w8, 0x000F000Fu, 0x64086408u, kMaskedXor));
+  o[3] = bitcast<f16x2>(__builtin_amdgcn_bitop3_b32(w8, 0x00F000F0u, 0x64806480u, kMaskedXor));
+}
+
+// E4M3 bytes at bits [8,16) and [24,32) of y -> fp16 pair holding value / 256
+// (exact, subnormal for the smallest codes).
+__device__ __forceinline__ f16x2 e4m3_hi_bytes_to_f16x2_raw(uint32_t y) {
+  return bitcast<f16x2>((y & 0x80008000u) | ((y >> 1) & 0x3F803F80u));
+}
+
 // E4M3 bytes placed at bits [8,16) and [24,32) of y -> fp16 pair (exact):
 // the fp16 with bits sign<<15 | (code&0x7F)<<7 equals value * 2^-8.
 __device__ __forceinline__ f16x2 e4m3_hi_bytes_to_f16x2(uint32_t y) {
