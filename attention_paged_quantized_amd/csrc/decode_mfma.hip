@@ -669,8 +669,7 @@ static void launch_split_nw(const AttnArgs& a, hipStream_t st) {
 template <int D, int KVF, int SM, typename TQ, int HW>
 static int launch_hw_q(const AttnArgs& a, hipStream_t st) {
   if (a.num_splits > 1) {
-    const long waves = (long)(a.hkv / HW) * a.batch * a.num_splits;
-    if (waves >= 8L * (a.num_cus > 0 ? a.num_cus : 256))
+    if (decode_split_waves(a.hkv, HW, a.batch, a.num_splits, a.num_cus) == 8)
       launch_split_nw<D, KVF, SM, TQ, HW, 8>(a, st);
     else
       launch_split_nw<D, KVF, SM, TQ, HW, 4>(a, st);
@@ -694,17 +693,13 @@ static int launch_hw(const AttnArgs& a, hipStream_t st) {
 template <int D, int KVF, int SM>
 static int launch_dq(const AttnArgs& a, hipStream_t st) {
   constexpr int C = KvGeom<KVF, D>::C;
-  if constexpr (C >= 128) {
-    return launch_hw<D, KVF, SM, 1>(a, st);
-  } else if constexpr (C == 64) {
-    if (a.hkv % 2 == 0) return launch_hw<D, KVF, SM, 2>(a, st);
-    return launch_hw<D, KVF, SM, 1>(a, st);
-  } else {
-    static_assert(C == 32, "row bytes");
-    if (a.hkv % 4 == 0) return launch_hw<D, KVF, SM, 4>(a, st);
-    if (a.hkv % 2 == 0) return launch_hw<D, KVF, SM, 2>(a, st);
-    return launch_hw<D, KVF, SM, 1>(a, st);
+  static_assert(C == 32 || C == 64 || C == 128, "row bytes");
+  switch (decode_heads_per_wave(KVF, D, a.hkv)) {
+    case 1: return launch_hw<D, KVF, SM, 1>(a, st);
+    case 2: if constexpr (C <= 64) return launch_hw<D, KVF, SM, 2>(a, st); break;
+    case 4: if constexpr (C <= 32) return launch_hw<D, KVF, SM, 4>(a, st); break;
   }
+  return -1;
 }
 
 template <int D>

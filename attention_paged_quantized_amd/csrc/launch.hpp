@@ -48,6 +48,32 @@ struct AttnArgs {
   float softmax_scale;  // already resolved (> 0)
 };
 
+// Launch geometry shared by the host planner and the launchers.
+// Decode (MFMA): one wave serves this many adjacent kv heads -- 128 / row
+// bytes when the kv head count allows, else the largest power of two that
+// divides it (row bytes: head_size, or head_size / 2 for INT4).
+inline int decode_heads_per_wave(int kv_format, int head_size, int hkv) {
+  const int row = (kv_format == 1 /* INT4 */) ? head_size / 2 : head_size;
+  int hw = row >= 128 ? 1 : 128 / row;
+  while (hw > 1 && hkv % hw) hw /= 2;
+  return hw;
+}
+// Decode split-KV: waves (one per chunk) per workgroup -- 8 when the grid
+// still gives every compute unit a workgroup, else 4.
+inline int decode_split_waves(int hkv, int heads_per_wave, int batch, int splits, int num_cus) {
+  const long waves = (long)(hkv / heads_per_wave) * batch * splits;
+  return waves >= 8L * (num_cus > 0 ? num_cus : 256) ? 8 : 4;
+}
+// Prefill (MFMA): workgroups of 4 waves x 32 / group tokens; a 1-D grid of
+// query tiles x kv heads x sequences, rounded up to a multiple of the 8 XCDs.
+constexpr int kPrefillWaves = 4;
+inline int prefill_tokens_per_workgroup(int group) { return kPrefillWaves * (32 / group); }
+inline int prefill_grid(int max_query_len, int group, int hkv, int batch) {
+  const int tok = prefill_tokens_per_workgroup(group);
+  const long units = (long)((max_query_len + tok - 1) / tok) * hkv * batch;
+  return (int)(8 * ((units + 7) / 8));
+}
+
 int launch_quant_append(const AppendArgs& a, hipStream_t st);
 int launch_decode_f32(const AttnArgs& a, hipStream_t st);     // any q_len (portable)
 int launch_decode_mfma(const AttnArgs& a, hipStream_t st);    // q_len in {0,1}

@@ -175,9 +175,12 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
   p->num_splits = S;
   if (mfma) {
     p->path = S > 1 ? PAQ_PATH_SPLIT : PAQ_PATH_SINGLE;
-    p->grid_x = d->kv_num_heads;
+    const int hw = paq::decode_heads_per_wave(d->kv_format, d->head_size, d->kv_num_heads);
+    p->grid_x = d->kv_num_heads / hw;
     p->grid_y = d->batch;
-    p->grid_z = S;
+    p->grid_z = S > 1 ? (S + paq::decode_split_waves(d->kv_num_heads, hw, d->batch, S, num_cus) -
+                         1) / paq::decode_split_waves(d->kv_num_heads, hw, d->batch, S, num_cus)
+                      : 1;
   } else {
     p->path = S > 1 ? PAQ_PATH_F32_SPLIT : PAQ_PATH_F32_SINGLE;
     p->grid_x = d->token_count;
@@ -210,9 +213,9 @@ int plan_prefill(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pa
   if (d->q_dtype != PAQ_DT_F32 &&
       paq::prefill_mfma_supports(d->head_size, group, d->block_size, d->q_dtype)) {
     p->path = PAQ_PATH_PREFILL;
-    p->grid_x = 0;                     // filled by the launcher's tile size
-    p->grid_y = d->kv_num_heads;
-    p->grid_z = d->batch;
+    p->grid_x = paq::prefill_grid(st.max_q, group, d->kv_num_heads, d->batch);
+    p->grid_y = 1;
+    p->grid_z = 1;
   } else {
     p->path = PAQ_PATH_F32_PREFILL;
     p->grid_x = d->token_count;

@@ -1,11 +1,14 @@
 // prefill_mfma.hip -- ragged, causal, chunked prefill over an INT8 / packed-INT4
 // / FP8 paged cache on gfx950 matrix cores (v_mfma_f32_32x32x16).
 //
-// Grid (query tiles, kv heads, sequences), sized from the exact max_query_len
-// of the host cum_q ("PagedAttention FA path: exact max_query_len", section
-// 1); a tile past its sequence's q_len exits at once, so zero-token sequences
-// cost one early exit.  Query tiles run heaviest-first (the last tiles of a
-// sequence see the most keys).
+// Work units (query tile, kv head, sequence), as many query tiles as the exact
+// max_query_len of the host cum_q needs ("PagedAttention FA path: exact
+// max_query_len", section 1); a tile past its sequence's q_len exits at once,
+// so zero-token sequences cost one early exit.  The 1-D grid is ordered for
+// the 8 XCDs: workgroup i runs on XCD i % 8, and each XCD takes a contiguous
+// range of (sequence, kv head) pairs, so the query tiles of a pair re-read its
+// keys and values from one L2; within a pair the heaviest tiles (the last
+// ones, which see the most keys) run first.
 //
 // Workgroup = 4 waves = 32/G tokens per wave x the G query heads of one kv head:
 // the GQA group is packed into the 32 MFMA query columns of every wave.
@@ -43,7 +46,7 @@ namespace paq {
 namespace {
 
 constexpr int kBN = 64;                      // keys per KV tile
-constexpr int kPfWavesPerGroup = 4;          // waves per workgroup (32/G tokens each)
+constexpr int kPfWavesPerGroup = kPrefillWaves;   // waves per workgroup (32/G tokens each)
 constexpr float kPfSlack = 8.0f;             // lazy running-max slack (log2 units)
 constexpr float kPfPScaleLog2 = 7.0f;        // fp16 P = p * 2^7
 
@@ -185,8 +188,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int G = a.num_heads / a.hkv;
   const int TPW = 32 / G;                       // tokens per wave
   const int TOK = kPfWaves * TPW;               // tokens per workgroup
-  const int qt = gridDim.x - 1 - blockIdx.x;    // heaviest tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Workgroup i is dispatched to XCD i % 8.  Each XCD gets a contiguous range
+  // of (sequence, kv head) pairs, so all query tiles of a pair share that
+  // XCD's L2 when they re-read the pair's keys and values; within the range,
+  // a pair's heaviest tiles come first.
+  const int ntq = (a.max_query_len + TOK - 1) / TOK;          // query tiles per pair
+  const int nunits = ntq * a.hkv * a.batch;
+  const int per_xcd = (nunits + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (u >= nunits) return;
+  const int qt = ntq - 1 - u % ntq;
+  const int h = (u / ntq) % a.hkv, b = (u / ntq) / a.hkv;
   const int q0 = a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - q0;
   const int tok0 = qt * TOK;
@@ -520,7 +532,8 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = kPfWavesPerGroup;
   const int G = a.num_heads / a.hkv;
   const int TOK = NW * (32 / G);
-  dim3 grid((a.max_query_len + TOK - 1) / TOK, a.hkv, a.batch);
+  static_assert(NW == kPrefillWaves, "prefill geometry");
+  dim3 grid(prefill_grid(a.max_query_len, G, a.hkv, a.batch), 1, 1);
   hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW>), grid, dim3(NW * 64), 0, st,
                      a, a.block_table);
   return 0;

@@ -60,7 +60,9 @@ def test_plan_decode_paths_and_workspace():
     # long INT4 decode with 128 chunks: workspace = T*H*S*(D+1) fp32 (aligned)
     d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
     p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 128, 256)
-    assert p.num_splits == 128 and p.grid_z == 128
+    # one wave per chunk and per pair of INT4 kv heads (a 128-byte line), 8 waves
+    # per workgroup: grid (8 / 2, 4, 128 / 8)
+    assert p.num_splits == 128 and (p.grid_x, p.grid_y, p.grid_z) == (4, 4, 16)
     assert p.workspace_bytes == 4 * 32 * 128 * 128 * 4 + 4 * 32 * 128 * 4
     assert paq.paged_attn_decode_workspace_size(d, _cum([1] * 4), [32768] * 4, 128) == \
         p.workspace_bytes
@@ -82,6 +84,12 @@ def test_plan_prefill_uses_exact_max_query_len():
     d = _desc(3, 5, mb=4)
     p = paq.paq_plan_prefill(d, _cum([5, 0, 0]), [0, 7, 3])
     assert p.max_query_len == 5 and p.active_seqs == 1
+    # one 32-token query tile (4 waves x 8 tokens at group 4) per (sequence, kv
+    # head): 1 x 8 x 3 = 24 workgroups, rounded up to the 8 XCDs
+    assert (p.grid_x, p.grid_y, p.grid_z) == (24, 1, 1)
+    # the exact maximum sizes the grid: 2048 tokens -> 64 query tiles per pair
+    p = paq.paq_plan_prefill(_desc(4, 8192, mb=128), _cum([2048] * 4), [0] * 4)
+    assert p.grid_x == 64 * 8 * 4
     # {1,0,0,0}: the heuristic would be -2 (an invalid grid)
     p = paq.paq_plan_prefill(_desc(4, 1, mb=4), _cum([1, 0, 0, 0]), [3, 0, 0, 0])
     assert p.max_query_len == 1
