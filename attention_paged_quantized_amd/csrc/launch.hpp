@@ -65,13 +65,13 @@ inline int decode_split_waves(int hkv, int heads_per_wave, int batch, int splits
   return waves >= 8L * (num_cus > 0 ? num_cus : 256) ? 8 : 4;
 }
 // Prefill (MFMA): workgroups of 4 waves x 32 / group tokens; a 1-D grid of
-// query tiles x kv heads x sequences, rounded up to a multiple of the 8 XCDs.
+// 8 XCDs x ceil(pairs / 8) (sequence, kv head) pairs x query tiles per pair.
 constexpr int kPrefillWaves = 4;
 inline int prefill_tokens_per_workgroup(int group) { return kPrefillWaves * (32 / group); }
 inline int prefill_grid(int max_query_len, int group, int hkv, int batch) {
   const int tok = prefill_tokens_per_workgroup(group);
-  const long units = (long)((max_query_len + tok - 1) / tok) * hkv * batch;
-  return (int)(8 * ((units + 7) / 8));
+  const long pairs = (long)hkv * batch;
+  return (int)(8 * ((pairs + 7) / 8) * ((max_query_len + tok - 1) / tok));
 }
 
 int launch_quant_append(const AppendArgs& a, hipStream_t st);

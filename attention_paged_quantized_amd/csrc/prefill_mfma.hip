@@ -5,10 +5,11 @@
 // max_query_len of the host cum_q needs ("PagedAttention FA path: exact
 // max_query_len", section 1); a tile past its sequence's q_len exits at once,
 // so zero-token sequences cost one early exit.  The 1-D grid is ordered for
-// the 8 XCDs: workgroup i runs on XCD i % 8, and each XCD takes a contiguous
-// range of (sequence, kv head) pairs, so the query tiles of a pair re-read its
-// keys and values from one L2; within a pair the heaviest tiles (the last
-// ones, which see the most keys) run first.
+// the 8 XCDs: workgroup i runs on XCD i % 8, and XCD x takes every 8th
+// (sequence, kv head) pair, so the query tiles of a pair re-read its keys and
+// values from one L2 and ragged sequences spread evenly over the XCDs; within
+// a pair the heaviest tiles (the last ones, which see the most keys) run
+// first.
 //
 // Workgroup = 4 waves = 32/G tokens per wave x the G query heads of one kv head:
 // the GQA group is packed into the 32 MFMA query columns of every wave.
@@ -188,17 +189,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int G = a.num_heads / a.hkv;
   const int TPW = 32 / G;                       // tokens per wave
   const int TOK = kPfWaves * TPW;               // tokens per workgroup
-  // Workgroup i is dispatched to XCD i % 8.  Each XCD gets a contiguous range
-  // of (sequence, kv head) pairs, so all query tiles of a pair share that
-  // XCD's L2 when they re-read the pair's keys and values; within the range,
-  // a pair's heaviest tiles come first.
+  // Workgroup i is dispatched to XCD i % 8.  XCD x takes the (sequence, kv
+  // head) pairs x, x + 8, x + 16, ... (with 8 kv heads: one head of every
+  // sequence, which balances ragged batches across XCDs); all query tiles of a
+  // pair run on its XCD and re-read the pair's keys and values from that L2,
+  // the pair's heaviest tiles first.
   const int ntq = (a.max_query_len + TOK - 1) / TOK;          // query tiles per pair
-  const int nunits = ntq * a.hkv * a.batch;
-  const int per_xcd = (nunits + 7) / 8;
-  const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (u >= nunits) return;
-  const int qt = ntq - 1 - u % ntq;
-  const int h = (u / ntq) % a.hkv, b = (u / ntq) / a.hkv;
+  const int k = (int)(blockIdx.x / 8);
+  const int pair = (int)(blockIdx.x % 8) + 8 * (k / ntq);
+  if (pair >= a.hkv * a.batch) return;
+  const int qt = ntq - 1 - k % ntq;
+  const int h = pair % a.hkv, b = pair / a.hkv;
   const int q0 = a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - q0;
   const int tok0 = qt * TOK;
