@@ -371,6 +371,10 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
   f16x8 pop;
 #pragma unroll
   for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(fmaf(v[i], c2, bias));
+  if (__builtin_expect(__ballot(fabsf(st.m) > kHugeScoreLog2) != 0, 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(mul_rn(v[i], c2) + bias);
+  }
   const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
   float l0 = __builtin_amdgcn_fdot2((f16x2){pop[0], pop[1]}, ones, st.l, false);
   float l1 = __builtin_amdgcn_fdot2((f16x2){pop[2], pop[3]}, ones, 0.f, false);

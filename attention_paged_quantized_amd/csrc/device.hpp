@@ -175,4 +175,19 @@ __device__ __forceinline__ float rows_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s * c rounded to fp32 on its own (never fused into a following add).
+__device__ __forceinline__ float mul_rn(float s, float c) {
+#pragma clang fp contract(off)
+  return s * c;
+}
+
+// Softmax numerators exp2(s * c - m + bias_extra), written as
+// exp2(fma(s, c, bias)) with bias = bias_extra - m.  The fused form mixes the
+// exact product with the running maximum m, which is a rounded product; once
+// |m| exceeds 2^38 the maximum's own rounding residual can exceed the 2^15
+// headroom of an fp16 P.  Scores that large (key scales far beyond the 16-bit
+// ranges, a hard-argmax softmax) take the product rounded first, exactly as
+// the maximum was, so the largest score maps to exp2(bias_extra) again.
+constexpr float kHugeScoreLog2 = 0x1p38f;
+
 }  // namespace paq

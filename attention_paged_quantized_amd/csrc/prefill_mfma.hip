@@ -437,6 +437,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
+    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) != 0, 0)) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(mul_rn(s[st][r], c2) + bias);
+    }
     {
       const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
       float lp[4] = {0.f, 0.f, 0.f, 0.f};

@@ -48,7 +48,12 @@
  * paq_last_error() describes the most recent failure of the calling thread.
  * Preconditions that are NOT checked (device-resident data): block ids in
  * [0, num_blocks), device cum_q/past_lens equal to their host copies, finite
- * positive scales, finite inputs.
+ * positive scales, finite inputs.  Key scales may lie far outside the 16-bit
+ * ranges (tested over [2^-60, 2^100] per channel): the 16-bit kernels fold
+ * k_scale / M into the query with M the power of two >= the kv head's largest
+ * key scale, and keep softmax_scale * M in fp32; the products
+ * softmax_scale * k_scale * |q . k codes| must stay below ~2^120.  Value
+ * scales must keep the outputs inside the query dtype's range.
  */
 #ifndef PAQ_H
 #define PAQ_H

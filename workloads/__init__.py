@@ -118,7 +118,8 @@ def make(name, seed=None):
 
 def _finish(name, rng, seed, *, batch, H, Hkv, D, bs, past, qlen, q_dtype, kv_format,
             scale_mode, kv_in_dtype, num_splits, kind, spare=8, num_blocks=None,
-            block_table=None, gains=True, key_scale_override=None, max_blocks=None):
+            block_table=None, gains=True, key_scale_override=None, key_code_sigma=2.0,
+            max_blocks=None):
     past = np.asarray(past, dtype=np.int32)
     qlen = np.asarray(qlen, dtype=np.int32)
     kv_lens = past + qlen
@@ -136,7 +137,9 @@ def _finish(name, rng, seed, *, batch, H, Hkv, D, bs, past, qlen, q_dtype, kv_fo
     vg = rng.lognormal(0.0, 0.5, (Hkv, D)) if gains else np.ones((Hkv, D))
     if key_scale_override is not None:
         k_scale = key_scale_override.astype(np.float32)
-        kall = 2.0 * k_scale.astype(np.float64)[None] * rng.standard_normal((P + T, Hkv, D))
+        ks = k_scale.astype(np.float64)
+        ks = ks[None] if ks.ndim == 2 else ks[None, :, None]
+        kall = key_code_sigma * ks * rng.standard_normal((P + T, Hkv, D))
     else:
         kall = rng.standard_normal((P + T, Hkv, D)) * kg[None]
     vall = rng.standard_normal((P + T, Hkv, D)) * vg[None]
@@ -236,12 +239,16 @@ NAMES = tuple(_BUILDERS)
 
 def custom(name, seed, *, batch, num_heads, kv_num_heads, head_size, block_size,
            past, q_lens, q_dtype, kv_format, scale_mode="channel", kv_in_dtype=None,
-           num_splits=1, kind="decode", spare=4):
-    """A workload with explicit structure, for edge-case tests."""
+           num_splits=1, kind="decode", spare=4, key_scale=None, key_code_sigma=2.0):
+    """A workload with explicit structure, for edge-case tests.  `key_scale`
+    (fp32, (kv_num_heads, head_size) or (kv_num_heads,)) replaces the
+    calibrated key scales; keys are then drawn as key_code_sigma * scale * N(0,1)
+    in kv_in_dtype (use "f32" for scales outside the 16-bit ranges)."""
     rng = np.random.default_rng(seed)
     return _finish(name, rng, seed, batch=batch, H=num_heads, Hkv=kv_num_heads,
                    D=head_size, bs=block_size, past=past, qlen=q_lens, q_dtype=q_dtype,
                    kv_format=kv_format, scale_mode=scale_mode,
                    kv_in_dtype=kv_in_dtype or ("f32" if q_dtype == "f32" else q_dtype),
                    num_splits=num_splits, kind=kind, spare=spare,
-                   gains=kv_format != "fp8")
+                   gains=kv_format != "fp8", key_scale_override=key_scale,
+                   key_code_sigma=key_code_sigma)
