@@ -356,8 +356,9 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
   // The reference maximum of a column is shared by its four lane rows and only
   // moves when a score exceeds it by more than kMaxSlack (log2 units): then the
   // rows exchange their maxima and the accumulators are rescaled.  Otherwise
-  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^7-scaled fp16 P holds.
-  if (__ballot(lm > st.m + kMaxSlack)) {
+  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^7-scaled fp16 P holds.  (The
+  // difference is exact near m, where m + kMaxSlack might round up.)
+  if (__ballot(lm - st.m > kMaxSlack)) {
     const float m_new = fmaxf(st.m, rows_max(lm));
     const float alpha = fast_exp2(st.m - m_new);         // 0 on the first update
     st.m = m_new;
@@ -369,11 +370,12 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
   // values (two per dot), which the value unbiasing in the epilogue relies on
   const float bias = kPScaleLog2 - st.m;
   f16x8 pop;
+  if (__builtin_expect(__ballot(fabsf(st.m) > kHugeScoreLog2) == 0, 1)) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(fmaf(v[i], c2, bias));
-  if (__builtin_expect(__ballot(fabsf(st.m) > kHugeScoreLog2) != 0, 0)) {
+    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(fmaf(v[i], c2, bias));
+  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(mul_rn(v[i], c2) + bias);
+    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(huge_score_arg(v[i], c2, st.m, kPScaleLog2));
   }
   const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
   float l0 = __builtin_amdgcn_fdot2((f16x2){pop[0], pop[1]}, ones, st.l, false);

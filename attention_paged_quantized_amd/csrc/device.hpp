@@ -175,19 +175,18 @@ __device__ __forceinline__ float rows_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// s * c rounded to fp32 on its own (never fused into a following add).
-__device__ __forceinline__ float mul_rn(float s, float c) {
+// Softmax numerators 2^(s*c - m + e) in an fp16 P, with m the running maximum
+// (in log2 units, a rounded product s*c) and e the scale exponent of P.
+// Below |m| = kHugeScoreLog2 they are computed as exp2(fma(s, c, e - m)): the
+// exact product against m and the rounding of e - m each stay within 1/8, so
+// with the lazy-maximum slack the argument stays under 15.5 and P under 2^16.
+// Past it (key scales far beyond the 16-bit ranges, a hard-argmax softmax) the
+// product is rounded first, as the maximum was, and the difference to m is
+// taken before adding e: exact near the maximum at every magnitude.
+constexpr float kHugeScoreLog2 = 0x1p22f;
+__device__ __forceinline__ float huge_score_arg(float s, float c, float m, float e) {
 #pragma clang fp contract(off)
-  return s * c;
+  return (s * c - m) + e;
 }
-
-// Softmax numerators exp2(s * c - m + bias_extra), written as
-// exp2(fma(s, c, bias)) with bias = bias_extra - m.  The fused form mixes the
-// exact product with the running maximum m, which is a rounded product; once
-// |m| exceeds 2^38 the maximum's own rounding residual can exceed the 2^15
-// headroom of an fp16 P.  Scores that large (key scales far beyond the 16-bit
-// ranges, a hard-argmax softmax) take the product rounded first, exactly as
-// the maximum was, so the largest score maps to exp2(bias_extra) again.
-constexpr float kHugeScoreLog2 = 0x1p38f;
 
 }  // namespace paq

@@ -117,27 +117,23 @@ __device__ __forceinline__ void decode_unit<KV_INT4, f16>(const u32x4& w, uint32
     out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p67) - bias);
   }
 }
-// FP8 E4M3 -> fp16 (exact): packed OCP-E4M3 -> fp32, then fp32 -> fp16
+// FP8 E4M3 -> fp16 / bf16 (exact: every E4M3 value, subnormals included, is
+// representable in both): gfx950's scaled packed conversion takes the two codes
+// of one 16-bit half of a word, with a unit scale
 template <>
 __device__ __forceinline__ void decode_unit<KV_FP8, f16>(const u32x4& w, uint32_t (&out)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
-    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
-    out[2 * i] = __builtin_bit_cast(uint32_t, (f16x2){(f16)f0[0], (f16)f0[1]});
-    out[2 * i + 1] = __builtin_bit_cast(uint32_t, (f16x2){(f16)f1[0], (f16)f1[1]});
+    out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
   }
 }
-// FP8 E4M3 -> bf16 (exact): gfx950's packed OCP-E4M3 -> fp32 conversion, then
-// fp32 -> bf16 (the values have 3 mantissa bits, so no rounding happens)
 template <>
 __device__ __forceinline__ void decode_unit<KV_FP8, bf16>(const u32x4& w, uint32_t (&out)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);   // bytes 0, 1
-    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);    // bytes 2, 3
-    out[2 * i] = __builtin_bit_cast(uint32_t, (bf16x2){(bf16)f0[0], (bf16)f0[1]});
-    out[2 * i + 1] = __builtin_bit_cast(uint32_t, (bf16x2){(bf16)f1[0], (bf16)f1[1]});
+    out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
   }
 }
 // bf16 QK is only used with FP8 per-head scales; the other formats never ask
@@ -164,6 +160,11 @@ __device__ __forceinline__ void decode_unit<KV_INT4, bf16>(const u32x4& w, uint3
       const bf16 b = (bf16)(float)((int)((byte >> 4) ^ 8u) - 8);
       out[4 * i + j] = __builtin_bit_cast(uint32_t, (bf16x2){a, b});
     }
+}
+
+// a if c else b, computed on the values
+__device__ __forceinline__ int32_t choose(bool c, int32_t a, int32_t b) {
+  return b ^ ((a ^ b) & -(int32_t)c);
 }
 
 // Position of key k (0..63) of a tile inside a V^T row: within each 16-key
@@ -224,71 +225,89 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // ---- staging: codes of a tile -> registers -> converted LDS tile ----
   // The physical blocks of a 64-key tile (at most 4 with 16-token blocks) are
   // wave-uniform, so they are fetched with scalar loads one tile ahead.
+  // Blocks past the sequence's last one are clamped to it and rows are taken
+  // within their block, so every load stays inside an allocated block; keys
+  // past kv_end read whatever the block holds there: their scores are masked
+  // and their value codes are zeroed before conversion.
+  static_assert(kBN == 16 * kPfWaves, "each wave stages 16 keys of a tile");
+  static_assert(Geo::VU_PER_T == 1, "one key pair x 16-byte unit of V per thread");
   const int nbt = (kBN >> lbs) > 0 ? (kBN >> lbs) : 1;       // blocks per tile (<= 4)
   const int last_blk = (kv_end - 1) >> lbs;
-  struct TileBlocks { int32_t b[4]; };
+  const uint32_t blk_bytes = (uint32_t)bs * row_stride;
+  // (the choices below are made on values with choose(): a conditional
+  // expression on the fields lets the compiler pick a field address instead,
+  // which keeps the struct in scratch memory)
+  struct TileBlocks { int32_t b0, b1, b2, b3; };
   auto tile_blocks = [&](int kt) {
-    TileBlocks t;
     const int first = (kt * kBN) >> lbs;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t.b[j] = table[min(first + min(j, nbt - 1), last_blk)];
-    return t;
+    return TileBlocks{table[min(first, last_blk)], table[min(first + min(1, nbt - 1), last_blk)],
+                      table[min(first + min(2, nbt - 1), last_blk)],
+                      table[min(first + min(3, nbt - 1), last_blk)]};
   };
-  auto row_off = [&](const TileBlocks& tb, int kt, int k) -> size_t {
-    const int key = min(kt * kBN + k, kv_end - 1);
-    const int j = (key >> lbs) - ((kt * kBN) >> lbs);      // 0..nbt-1
-    const int32_t blk = j == 0 ? tb.b[0] : j == 1 ? tb.b[1] : j == 2 ? tb.b[2] : tb.b[3];
-    return ((size_t)blk << lbs | (key & (bs - 1))) * row_stride;
+  // K: wave w stages keys [16w, 16w + 16) of a tile, which lie in one block
+  // for every supported block size: the block is wave-uniform and a lane's
+  // offset into it is constant.  KL loads per lane, 64/UPR keys per load.
+  constexpr int KL = Geo::UPR >= 4 ? Geo::UPR / 4 : 1;
+  constexpr int KPL = 64 / Geo::UPR;                           // keys per load
+  const bool k_active = Geo::UPR >= 4 || lane < 16 * Geo::UPR;
+  uint32_t koff[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i)
+    koff[i] = (uint32_t)(i * KPL + lane / Geo::UPR) * row_stride + 16 * (lane % Geo::UPR);
+  auto k_base = [&](const TileBlocks& tb, int kt) -> const uint8_t* {
+    const int key = kt * kBN + 16 * wave;
+    const int j = (key >> lbs) - ((kt * kBN) >> lbs);         // 0..3, uniform
+    const int32_t blk =
+        choose(j >= 3, tb.b3, choose(j >= 2, tb.b2, choose(j >= 1, tb.b1, tb.b0)));
+    return kbase + ((size_t)blk * bs + (key & (bs - 1))) * row_stride;
+  };
+  // V: thread t stages keys 2m, 2m+1 (m = t % 32) of 16-byte unit t / 32; the
+  // 32 key pairs of a wave span the whole tile, so the block is chosen per lane
+  // from the tile's (at most 4) blocks.
+  const int vm = tid % (kBN / 2), vc = tid / (kBN / 2);
+  const bool v_active = Geo::VUNITS % kPfThreads == 0 || tid < Geo::VUNITS;
+  const int vj = bs <= kBN ? (2 * vm) >> lbs : 0;
+  const uint32_t voff = (uint32_t)(bs <= kBN ? (2 * vm) & (bs - 1) : 2 * vm) * row_stride + 16 * vc;
+  auto v_addr = [&](const TileBlocks& tb, int kt) -> const uint8_t* {
+    const int r0 = bs > kBN ? (kt * kBN) & (bs - 1) : 0;      // tile's first row in its block
+    const int32_t blk =
+        choose(vj >= 3, tb.b3, choose(vj >= 2, tb.b2, choose(vj >= 1, tb.b1, tb.b0)));
+    return vbase + (size_t)r0 * row_stride + (size_t)(uint32_t)blk * blk_bytes + voff;
   };
   // raw codes of one tile, held by this thread (two sets: tiles kt+1 and kt+2
   // are in flight while tile kt is computed)
-  // The load addresses are kept in the set and stay live until the set is
-  // stored: otherwise the compiler may hand their registers to the MFMA
+  // The V load address is kept in the set and stays live until the set is
+  // stored: otherwise the compiler may hand its registers to the MFMA
   // accumulators of the current tile and then drain the loads to avoid
   // overwriting a vector-memory source operand.
   struct RawSet {
-    u32x4 k[Geo::KU_PER_T];
-    u32x4 v[Geo::VU_PER_T][2];
-    const uint8_t* ka[Geo::KU_PER_T];
-    const uint8_t* va[Geo::VU_PER_T][2];
+    u32x4 k[KL];
+    u32x4 v[2];
+    const uint8_t* va;
+    int kt;
   };
   auto load_codes = [&](RawSet& rs, const TileBlocks& tb, int kt) {
+    rs.kt = kt;
+    const uint8_t* kb = k_base(tb, kt);
+    if (k_active) {
 #pragma unroll
-    for (int i = 0; i < Geo::KU_PER_T; ++i) {
-      const int u = tid + i * kPfThreads;
-      if (Geo::KUNITS % kPfThreads && u >= Geo::KUNITS) break;
-      const int k = u / Geo::UPR, c = u % Geo::UPR;
-      rs.ka[i] = kbase + row_off(tb, kt, k) + 16 * c;
-      rs.k[i] = *reinterpret_cast<const u32x4*>(rs.ka[i]);
+      for (int i = 0; i < KL; ++i) rs.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
     }
-#pragma unroll
-    for (int i = 0; i < Geo::VU_PER_T; ++i) {
-      const int u = tid + i * kPfThreads;
-      if (Geo::VUNITS % kPfThreads && u >= Geo::VUNITS) break;
-      const int m = u % (kBN / 2), c = u / (kBN / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        rs.va[i][e] = vbase + row_off(tb, kt, 2 * m + e) + 16 * c;
-        rs.v[i][e] = *reinterpret_cast<const u32x4*>(rs.va[i][e]);
-      }
+    rs.va = v_addr(tb, kt);
+    if (v_active) {
+      rs.v[0] = *reinterpret_cast<const u32x4*>(rs.va);
+      rs.v[1] = *reinterpret_cast<const u32x4*>(rs.va + row_stride);
     }
-  };
-  auto keep_addresses = [&](const RawSet& rs) {
-#pragma unroll
-    for (int i = 0; i < Geo::KU_PER_T; ++i) asm volatile("" ::"v"(rs.ka[i]));
-#pragma unroll
-    for (int i = 0; i < Geo::VU_PER_T; ++i) asm volatile("" ::"v"(rs.va[i][0]), "v"(rs.va[i][1]));
   };
   // Convert the codes of a tile into LDS buffer `buf`: K rows (store_k) and
   // V^T rows (store_v), done beside the QK and the PV products respectively.
   auto store_k = [&](const RawSet& rs, int buf) {
-    keep_addresses(rs);
-    uint8_t* kl = lds[buf];
+    asm volatile("" ::"v"(rs.va));
+    if (!k_active) return;
+    uint8_t* kl = lds[buf] + (16 * wave) * Geo::KROW;
 #pragma unroll
-    for (int i = 0; i < Geo::KU_PER_T; ++i) {
-      const int u = tid + i * kPfThreads;
-      if (Geo::KUNITS % kPfThreads && u >= Geo::KUNITS) break;
-      const int k = u / Geo::UPR, c = u % Geo::UPR;
+    for (int i = 0; i < KL; ++i) {
+      const int k = i * KPL + lane / Geo::UPR, c = lane % Geo::UPR;
       uint32_t w[Geo::CPU / 2];
       decode_unit<KVF, TK>(rs.k[i], w);
       // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
@@ -299,26 +318,27 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     }
   };
   auto store_v = [&](const RawSet& rs, int buf) {
-    keep_addresses(rs);
+    asm volatile("" ::"v"(rs.va));
+    if (!v_active) return;
     uint8_t* vl = lds[buf] + kBN * Geo::KROW;
+    u32x4 v0 = rs.v[0], v1 = rs.v[1];
+    if ((rs.kt + 1) * kBN > kv_end) {              // tile reaches past the last key
+      const int key = rs.kt * kBN + 2 * vm;
+      if (key >= kv_end) v0 = (u32x4){0u, 0u, 0u, 0u};
+      if (key + 1 >= kv_end) v1 = (u32x4){0u, 0u, 0u, 0u};
+    }
+    // consecutive lanes take consecutive key pairs of one 16-byte unit: the
+    // 32 lanes of a write then hit 32 different V^T-row banks
+    uint32_t w0[Geo::CPU / 2], w1[Geo::CPU / 2];
+    decode_unit<KVF, f16>(v0, w0);
+    decode_unit<KVF, f16>(v1, w1);
+    const int pos = vt_pos(2 * vm);                        // even: keys 2m, 2m+1 adjacent
 #pragma unroll
-    for (int i = 0; i < Geo::VU_PER_T; ++i) {
-      const int u = tid + i * kPfThreads;
-      if (Geo::VUNITS % kPfThreads && u >= Geo::VUNITS) break;
-      // consecutive lanes take consecutive key pairs of one 16-byte unit: the
-      // 32 lanes of a write then hit 32 different V^T-row banks
-      const int m = u % (kBN / 2), c = u / (kBN / 2);
-      uint32_t w0[Geo::CPU / 2], w1[Geo::CPU / 2];
-      decode_unit<KVF, f16>(rs.v[i][0], w0);
-      decode_unit<KVF, f16>(rs.v[i][1], w1);
-      const int pos = vt_pos(2 * m);                       // even: keys 2m, 2m+1 adjacent
-#pragma unroll
-      for (int j = 0; j < Geo::CPU; ++j) {
-        const int d = Geo::CPU * c + j;
-        // {key 2m, key 2m+1} of channel d: the matching halves of w0, w1
-        const uint32_t pair = perm(w1[j >> 1], w0[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 2 * pos) = pair;
-      }
+    for (int j = 0; j < Geo::CPU; ++j) {
+      const int d = Geo::CPU * vc + j;
+      // {key 2m, key 2m+1} of channel d: the matching halves of w0, w1
+      const uint32_t pair = perm(w1[j >> 1], w0[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 2 * pos) = pair;
     }
   };
 
@@ -406,21 +426,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // causal mask on raw scores, lazy running max in log2 units
-    const bool diag = key0 + kBN - 1 > past + tok0 + wave * TPW;   // may need masking
+    // causal mask on raw scores, only on tiles that cross this wave's diagonal
+    // (its first row clamped like the rows themselves, so a wave of padded
+    // rows masks the keys past the end too)
+    if (key0 + kBN - 1 > past + min(tok0 + wave * TPW, qlen - 1)) {
+      const int lim = row_lim - key0 - 4 * eta;     // last visible key offset (eta = 0)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[st][r] = 32 * st + 8 * (r >> 2) + (r & 3) <= lim ? s[st][r] : -INFINITY;
+    }
+    // lazy running max in log2 units (the difference is exact near m_run,
+    // where m_run + kPfSlack might round up)
     float lm = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (diag) {
-          const int key = key0 + 32 * st + 8 * (r >> 2) + 4 * eta + (r & 3);
-          s[st][r] = key <= row_lim ? s[st][r] : -INFINITY;
-        }
-        lm = fmaxf(lm, s[st][r]);
-      }
+      for (int r = 0; r < 16; ++r) lm = fmaxf(lm, s[st][r]);
     lm *= c2;
-    if (__ballot(lm > m_run + kPfSlack)) {
+    if (__ballot(lm - m_run > kPfSlack)) {
       const float m_new = fmaxf(m_run, fmaxf(lm, __shfl_xor(lm, 32, 64)));
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -430,19 +455,21 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     }
     // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
     // regs 8c..8c+7); l accumulates the same fp16 values, two per dot
-    const float bias = kPfPScaleLog2 - m_run;
     f16x8 p[4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
-    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) != 0, 0)) {
+    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) == 0, 1)) {
+      const float bias = kPfPScaleLog2 - m_run;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(mul_rn(s[st][r], c2) + bias);
+          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[2 * st + (r >> 3)][r & 7] =
+              (f16)fast_exp2(huge_score_arg(s[st][r], c2, m_run, kPfPScaleLog2));
     }
     {
       const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
