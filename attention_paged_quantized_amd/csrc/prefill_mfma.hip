@@ -39,6 +39,8 @@
 // per-head scales go into the score factor.  Value scales are applied in the
 // epilogue.  QK runs in fp16, or in bf16 for bf16 queries with per-head scales
 // (then both operands are exact); PV always runs in fp16 (codes are exact).
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -246,14 +248,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   };
   // K: wave w stages keys [16w, 16w + 16) of a tile, which lie in one block
   // for every supported block size: the block is wave-uniform and a lane's
-  // offset into it is constant.  KL loads per lane, 64/UPR keys per load.
+  // offset into it is constant.  KL loads per lane, KPL keys per load, lane l
+  // taking key l % KPL and 16-byte unit l / KPL of it: the row writes of such
+  // a load to LDS are free of bank conflicts (with the unit index running
+  // fastest over the lanes they are not).
   constexpr int KL = Geo::UPR >= 4 ? Geo::UPR / 4 : 1;
-  constexpr int KPL = 64 / Geo::UPR;                           // keys per load
+  constexpr int KPL = Geo::UPR >= 4 ? 64 / Geo::UPR : 16;      // keys per load
   const bool k_active = Geo::UPR >= 4 || lane < 16 * Geo::UPR;
+  const int kx = lane % KPL, kc = lane / KPL;                  // key, unit
   uint32_t koff[KL];
 #pragma unroll
-  for (int i = 0; i < KL; ++i)
-    koff[i] = (uint32_t)(i * KPL + lane / Geo::UPR) * row_stride + 16 * (lane % Geo::UPR);
+  for (int i = 0; i < KL; ++i) koff[i] = (uint32_t)(i * KPL + kx) * row_stride + 16 * kc;
   auto k_base = [&](const TileBlocks& tb, int kt) -> const uint8_t* {
     const int key = kt * kBN + 16 * wave;
     const int j = (key >> lbs) - ((kt * kBN) >> lbs);         // 0..3, uniform
@@ -274,80 +279,91 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
         choose(vj >= 3, tb.b3, choose(vj >= 2, tb.b2, choose(vj >= 1, tb.b1, tb.b0)));
     return vbase + (size_t)r0 * row_stride + (size_t)(uint32_t)blk * blk_bytes + voff;
   };
-  // raw codes of one tile, held by this thread (two sets: tiles kt+1 and kt+2
-  // are in flight while tile kt is computed)
-  // The V load address is kept in the set and stays live until the set is
-  // stored: otherwise the compiler may hand its registers to the MFMA
-  // accumulators of the current tile and then drain the loads to avoid
-  // overwriting a vector-memory source operand.
-  struct RawSet {
-    u32x4 k[KL];
-    u32x4 v[2];
-    const uint8_t* va;
-    int kt;
-  };
-  auto load_codes = [&](RawSet& rs, const TileBlocks& tb, int kt) {
-    rs.kt = kt;
+  // Raw codes of a tile, held by this thread between their load and their
+  // conversion into LDS one step later (K codes of tile t+3 and V codes of
+  // tile t+2 are loaded at the end of step t).  The V load address stays live
+  // until its set is converted: otherwise the compiler may hand its registers
+  // to MFMA accumulators and then drain the loads to avoid overwriting a
+  // vector-memory source operand.
+  struct RawK { u32x4 k[KL]; };
+  struct RawV { u32x4 v[2]; const uint8_t* va; int kt; };
+  auto load_k = [&](RawK& r, const TileBlocks& tb, int kt) {
     const uint8_t* kb = k_base(tb, kt);
     if (k_active) {
 #pragma unroll
-      for (int i = 0; i < KL; ++i) rs.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
-    }
-    rs.va = v_addr(tb, kt);
-    if (v_active) {
-      rs.v[0] = *reinterpret_cast<const u32x4*>(rs.va);
-      rs.v[1] = *reinterpret_cast<const u32x4*>(rs.va + row_stride);
+      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
     }
   };
-  // Convert the codes of a tile into LDS buffer `buf`: K rows (store_k) and
-  // V^T rows (store_v), done beside the QK and the PV products respectively.
-  auto store_k = [&](const RawSet& rs, int buf) {
-    asm volatile("" ::"v"(rs.va));
+  auto load_v = [&](RawV& r, const TileBlocks& tb, int kt) {
+    r.kt = kt;
+    r.va = v_addr(tb, kt);
+    if (v_active) {
+      r.v[0] = *reinterpret_cast<const u32x4*>(r.va);
+      r.v[1] = *reinterpret_cast<const u32x4*>(r.va + row_stride);
+    }
+  };
+  // Conversions into LDS buffer `buf`: the K rows of a tile (row-major) and
+  // its V^T rows (channel-major, keys in the PV operand order), in pieces that
+  // phase B spreads over its matrix products.
+  auto stage_k_unit = [&](const RawK& r, int buf, int i) {   // K unit i of this lane
     if (!k_active) return;
     uint8_t* kl = lds[buf] + (16 * wave) * Geo::KROW;
+    const int k = i * KPL + kx, c = kc;
+    uint32_t w[Geo::CPU / 2];
+    decode_unit<KVF, TK>(r.k[i], w);
+    // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int k = i * KPL + lane / Geo::UPR, c = lane % Geo::UPR;
-      uint32_t w[Geo::CPU / 2];
-      decode_unit<KVF, TK>(rs.k[i], w);
-      // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
-#pragma unroll
-      for (int j = 0; j < Geo::CPU / 8; ++j)
-        *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 2 * Geo::CPU * c + 16 * j) =
-            (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
-    }
+    for (int j = 0; j < Geo::CPU / 8; ++j)
+      *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 2 * Geo::CPU * c + 16 * j) =
+          (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
   };
-  auto store_v = [&](const RawSet& rs, int buf) {
-    asm volatile("" ::"v"(rs.va));
-    if (!v_active) return;
-    uint8_t* vl = lds[buf] + kBN * Geo::KROW;
-    u32x4 v0 = rs.v[0], v1 = rs.v[1];
-    if ((rs.kt + 1) * kBN > kv_end) {              // tile reaches past the last key
-      const int key = rs.kt * kBN + 2 * vm;
-      if (key >= kv_end) v0 = (u32x4){0u, 0u, 0u, 0u};
-      if (key + 1 >= kv_end) v1 = (u32x4){0u, 0u, 0u, 0u};
+  typedef uint32_t VWords[Geo::CPU / 2];
+  auto stage_v_decode = [&](const RawV& r, VWords& w0, VWords& w1) {
+    asm volatile("" ::"v"(r.va));
+    u32x4 v0 = r.v[0], v1 = r.v[1];
+    if constexpr (KVF == KV_FP8) {
+      // keys past kv_end hold whatever their block holds: E4M3 NaN codes
+      // there would survive the zero P (0 * NaN), so they become zeros
+      const int key = r.kt * kBN + 2 * vm;
+      v0 &= (u32x4)(key < kv_end ? ~0u : 0u);
+      v1 &= (u32x4)(key + 1 < kv_end ? ~0u : 0u);
     }
-    // consecutive lanes take consecutive key pairs of one 16-byte unit: the
-    // 32 lanes of a write then hit 32 different V^T-row banks
-    uint32_t w0[Geo::CPU / 2], w1[Geo::CPU / 2];
     decode_unit<KVF, f16>(v0, w0);
     decode_unit<KVF, f16>(v1, w1);
+  };
+  // V^T rows of channels CPU*vc + [j0, j1): consecutive lanes take consecutive
+  // key pairs of one 16-byte unit, so the 32 lanes of a write hit 32 banks
+  auto stage_v_write = [&](int buf, const VWords& w0, const VWords& w1, int j0, int j1) {
+    if (!v_active) return;
+    uint8_t* vl = lds[buf] + kBN * Geo::KROW;
     const int pos = vt_pos(2 * vm);                        // even: keys 2m, 2m+1 adjacent
 #pragma unroll
-    for (int j = 0; j < Geo::CPU; ++j) {
+    for (int j = j0; j < j1; ++j) {
       const int d = Geo::CPU * vc + j;
       // {key 2m, key 2m+1} of channel d: the matching halves of w0, w1
       const uint32_t pair = perm(w1[j >> 1], w0[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
       *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 2 * pos) = pair;
     }
   };
+  auto store_k = [&](const RawK& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) stage_k_unit(r, buf, i);
+  };
+  auto store_v = [&](const RawV& r, int buf) {
+    VWords w0, w1;
+    stage_v_decode(r, w0, w1);
+    stage_v_write(buf, w0, w1, 0, Geo::CPU);
+  };
 
-  RawSet ra, rb;
-  TileBlocks tb_next = tile_blocks(0);
-  load_codes(ra, tb_next, 0);
-  tb_next = tile_blocks(1);
-  load_codes(rb, tb_next, 1);
-  tb_next = tile_blocks(2);
+  // tiles 0 and 1 are converted before the first step; tile 2's K codes and
+  // tile 1's V codes are in registers when it starts
+  TileBlocks tbA = tile_blocks(0), tbB = tile_blocks(1);
+  RawK rk, rk1;
+  RawV rv;
+  load_k(rk, tbA, 0);
+  load_v(rv, tbA, 0);
+  load_k(rk1, tbB, 1);
+  const TileBlocks tb2 = tile_blocks(2);
 
   // ---- query operand: Q'^T columns, fold of the key scale ----
   const int my_tok = min(tok0 + wave * TPW + n / G, qlen - 1);      // clamp padded rows
@@ -356,7 +372,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   float Mh = 1.f;
   if constexpr (SM == SCALE_CHANNEL) {
     float smax = 0.f;
-    for (int d = lane; d < D; d += 64) smax = fmaxf(smax, fabsf(a.k_scale[h * D + d]));
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) smax = fmaxf(smax, fabsf(a.k_scale[h * D + lane + 64 * i]));
     smax = wave_max(smax);
     int ex;
     const float fr = frexpf(smax, &ex);
@@ -384,51 +401,31 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
 
-  // One 64-key tile: S^T = K Q'^T for two 32-key blocks, causal mask, lazy
-  // online softmax, O^T += V^T P^T.  The conversion of the next tile (codes in
-  // `nxt`) into the other LDS buffer runs beside the MFMAs: its K rows beside
-  // the QK products, its V^T rows beside the PV products.
   // (sched_group_barrier masks: 0x002 VALU, 0x008 MFMA, 0x100 LDS read,
-  // 0x200 LDS write)
-  auto compute = [&](int kt, const RawSet& nxt, int nbuf) {
-    const int buf = kt & 1;
-    const int key0 = kt * kBN;
-    const uint8_t* kl = lds[buf];
-    const uint8_t* vl = lds[buf] + kBN * Geo::KROW;
-    f32x16 s[2] = {(f32x16){}, (f32x16){}};
-    {
-      const uint8_t* k0p = kl + n * Geo::KROW + 16 * eta;
-      const uint8_t* k1p = k0p + 32 * Geo::KROW;
-      kvec ka[NKK];
-      __builtin_amdgcn_sched_barrier(0);
+  // 0x200 LDS write, 0x400 transcendental)
+  // S^T = K Q'^T of tile t (keys 0-31 in s[0], 32-63 in s[1]), from LDS
+  // buffer t & 1; the two accumulations alternate.
+  auto qk = [&](int t, f32x16 (&s)[2]) {
+    const uint8_t* k0p = lds[t & 1] + n * Geo::KROW + 16 * eta;
+    const uint8_t* k1p = k0p + 32 * Geo::KROW;
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) ka[kk] = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[0] = MK::run(ka[kk], qop[kk], s[0]);
-        ka[kk] = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[1] = MK::run(ka[kk], qop[kk], s[1]);
-      store_k(nxt, nbuf);
-      __builtin_amdgcn_sched_group_barrier(0x100, NKK, 0);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const kvec a0 = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
+      const kvec a1 = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
+      s[0] = MK::run(a0, qop[kk], s[0]);
+      s[1] = MK::run(a1, qop[kk], s[1]);
     }
-    // causal mask on raw scores, only on tiles that cross this wave's diagonal
-    // (its first row clamped like the rows themselves, so a wave of padded
-    // rows masks the keys past the end too)
+  };
+  // Causal mask of tile t (only where it crosses this wave's diagonal; the
+  // first row is clamped like the rows themselves, so a wave of padded rows
+  // masks the keys past the end too), then the lazy running maximum in log2
+  // units: the accumulators are rescaled only when a score exceeds it by more
+  // than kPfSlack (the difference is exact near m_run, where m_run + kPfSlack
+  // might round up).
+  auto mask_and_max = [&](int t, f32x16 (&s)[2]) {
+    const int key0 = t * kBN;
     if (key0 + kBN - 1 > past + min(tok0 + wave * TPW, qlen - 1)) {
       const int lim = row_lim - key0 - 4 * eta;     // last visible key offset (eta = 0)
 #pragma unroll
@@ -437,8 +434,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
         for (int r = 0; r < 16; ++r)
           s[st][r] = 32 * st + 8 * (r >> 2) + (r & 3) <= lim ? s[st][r] : -INFINITY;
     }
-    // lazy running max in log2 units (the difference is exact near m_run,
-    // where m_run + kPfSlack might round up)
     float lm = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -453,87 +448,144 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < NDT; ++i) o[i] *= alpha;
     }
-    // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
-    // regs 8c..8c+7); l accumulates the same fp16 values, two per dot
-    f16x8 p[4];
-    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) == 0, 1)) {
-      const float bias = kPfPScaleLog2 - m_run;
+  };
+  // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
+  // regs 8c..8c+7), and partial sums of the same fp16 values, two per dot.
+  auto exps = [&](const f32x16 (&s)[2], f16x8 (&p)[4], float (&lp)[4], bool huge) {
+    const float bias = kPfPScaleLog2 - m_run;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[2 * st + (r >> 3)][r & 7] = (f16)fast_exp2(fmaf(s[st][r], c2, bias));
-    } else {
+      for (int r = 0; r < 16; ++r)
+        p[2 * st + (r >> 3)][r & 7] =
+            huge ? (f16)fast_exp2(huge_score_arg(s[st][r], c2, m_run, kPfPScaleLog2))
+                 : (f16)fast_exp2(fmaf(s[st][r], c2, bias));
+    const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+    for (int i = 0; i < 4; ++i) lp[i] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[2 * st + (r >> 3)][r & 7] =
-              (f16)fast_exp2(huge_score_arg(s[st][r], c2, m_run, kPfPScaleLog2));
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lp[i] = __builtin_amdgcn_fdot2((f16x2){p[c][2 * i], p[c][2 * i + 1]}, ones, lp[i], false);
+  };
+  // The phases below are written as 16 bundles, each one matrix product plus
+  // the operand reads and vector work placed beside it; sched_barrier fences
+  // keep the bundles in order, so every product finds its operands already
+  // read (up to four LDS reads in flight) and the vector ALUs work while the
+  // matrix cores run.
+  //
+  // Phase A of step t: the QK product of tile t+1 (operand i: rows
+  // 32*(i%2)..+31, channels 16*(i/2)..+15; the two accumulations alternate)
+  // beside the exponentials of tile t, two scores per bundle.
+  auto phase_a = [&](auto do_qk, int t, const f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
+                     f16x8 (&p)[4], float (&lp)[4]) {
+    constexpr bool QK = decltype(do_qk)::value;
+    constexpr int NM = 2 * NKK;                     // products (16 for D = 128)
+    const float bias = kPfPScaleLog2 - m_run;
+    const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
+    const uint8_t* k0p = lds[(t + 1) & 1] + n * Geo::KROW + 16 * eta;
+    auto kaddr = [&](int i) { return k0p + (i & 1) * 32 * Geo::KROW + 32 * (i >> 1); };
+    kvec ka[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lp[i] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (QK) {
+      s_next[0] = (f32x16){};
+      s_next[1] = (f32x16){};
+#pragma unroll
+      for (int i = 0; i < 4 && i < NM; ++i) ka[i] = *reinterpret_cast<const kvec*>(kaddr(i));
     }
-    {
-      const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
-      float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          lp[i] = __builtin_amdgcn_fdot2((f16x2){p[c][2 * i], p[c][2 * i + 1]}, ones, lp[i],
-                                         false);
-      l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
-    }
-    // O^T += V^T P^T, with the V^T operands of the next channel tile read
-    // while the current tile's MFMAs run, beside the next tile's V^T staging
-    {
-      const uint8_t* vp = vl + n * Geo::VROW + 16 * eta;
-      f16x8 va[4];
+    for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * c);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c], p[c], o[dt], 0, 0, 0);
-          if (dt + 1 < NDT)
-            va[c] = *reinterpret_cast<const f16x8*>(vp + 32 * (dt + 1) * Geo::VROW + 32 * c);
+      if constexpr (QK) {
+        if (i < NM) {
+          s_next[i & 1] = MK::run(ka[i & 3], qop[i >> 1], s_next[i & 1]);
+          if (i + 4 < NM) ka[i & 3] = *reinterpret_cast<const kvec*>(kaddr(i + 4));
         }
       }
-      store_v(nxt, nbuf);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * (NDT - 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      // scores 2i, 2i+1 of this lane: block st, registers r, r+1
+      const int st = i >> 3, r = (2 * i) & 15;
+      const f16 e0 = (f16)fast_exp2(fmaf(s_cur[st][r], c2, bias));
+      const f16 e1 = (f16)fast_exp2(fmaf(s_cur[st][r + 1], c2, bias));
+      p[2 * st + (r >> 3)][r & 7] = e0;
+      p[2 * st + (r >> 3)][(r & 7) + 1] = e1;
+      lp[i & 3] = __builtin_amdgcn_fdot2((f16x2){e0, e1}, ones, lp[i & 3], false);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // Tile kt+1's codes are in registers and tile kt+2's are loading while tile
-  // kt is computed; tile kt+1 is converted into the other LDS buffer during
-  // the products of tile kt.  Loads past the last tile re-read its final keys
-  // (addresses are clamped) and their conversion lands in the idle buffer.
-  store_k(ra, 0);
-  store_v(ra, 0);
+  // Phase B of step t: O^T += V^T P^T for tile t (product i: channel tile
+  // i/4, key chunk i%4) beside the conversion of the K codes of tile t+2
+  // (into buffer t & 1) and the V codes of tile t+1 (into buffer (t+1) & 1),
+  // and then the loads of the codes of K(t+3) and V(t+2) into the same
+  // registers.
+  auto phase_b = [&](int t, const f16x8 (&p)[4], RawK& rk, RawV& rv, const TileBlocks& tbk,
+                     const TileBlocks& tbv) {
+    constexpr int NM = 4 * NDT;                     // products (16 for D = 128)
+    constexpr int VW = Geo::CPU / 8;                // V^T channels written per bundle
+    const uint8_t* vp = lds[t & 1] + kBN * Geo::KROW + n * Geo::VROW + 16 * eta;
+    auto vaddr = [&](int i) { return vp + 32 * (i >> 2) * Geo::VROW + 32 * (i & 3); };
+    f16x8 va[4];
+    VWords w0, w1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) va[i] = *reinterpret_cast<const f16x8*>(vaddr(i));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < NM) {
+        o[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 3], p[i & 3], o[i >> 2], 0, 0, 0);
+        if (i + 4 < NM) va[i & 3] = *reinterpret_cast<const f16x8*>(vaddr(i + 4));
+      }
+      if (i < KL) stage_k_unit(rk, t & 1, i);
+      if (i == KL) stage_v_decode(rv, w0, w1);
+      if (i > KL && i <= KL + 8) stage_v_write((t + 1) & 1, w0, w1, VW * (i - KL - 1), VW * (i - KL));
+      if (i == 15) {
+        load_k(rk, tbk, t + 3);
+        load_v(rv, tbv, t + 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Step t: mask/max/rescale of tile t, phase A, phase B (which also issues
+  // the loads of K(t+3) and V(t+2) once the codes it converts are read),
+  // barrier.  The conversions of step t write LDS regions no wave reads
+  // during step t (K(t) and V(t-1) were last read before the previous
+  // barrier), and what they write is read after this step's barrier.
+  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    mask_and_max(t, s_cur);
+    const TileBlocks tbC = tile_blocks(t + 4);
+    f16x8 p[4];
+    float lp[4];
+    if (t + 1 < ntiles)
+      phase_a(std::true_type{}, t, s_cur, s_next, p, lp);
+    else
+      phase_a(std::false_type{}, t, s_cur, s_next, p, lp);
+    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) != 0, 0))
+      exps(s_cur, p, lp, true);
+    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    phase_b(t, p, rk, rv, tbB, tbA);
+    __syncthreads();
+    tbA = tbB;
+    tbB = tbC;
+  };
+
+  store_k(rk, 0);
+  store_v(rv, 0);
+  store_k(rk1, 1);
+  load_k(rk, tb2, 2);
+  load_v(rv, tbB, 1);
+  tbA = tb2;
+  tbB = tile_blocks(3);
   __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk(0, sa);
+  __syncthreads();                 // buffer 0's K rows are rewritten in step 0
   for (int kt = 0; kt < ntiles; kt += 2) {
-    load_codes(ra, tb_next, kt + 2);
-    tb_next = tile_blocks(kt + 3);
-    compute(kt, rb, (kt + 1) & 1);
-    __syncthreads();
+    step(kt, sa, sb);
     if (kt + 1 >= ntiles) break;
-    load_codes(rb, tb_next, kt + 3);
-    tb_next = tile_blocks(kt + 4);
-    compute(kt + 1, ra, kt & 1);
-    __syncthreads();
+    step(kt + 1, sb, sa);
   }
 
   // ---- epilogue: normalise, value scale, store the rows of this wave ----

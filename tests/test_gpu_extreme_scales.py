@@ -5,7 +5,9 @@ dividing by the power of two M_h >= max|k_scale| of the kv head ("ONNX Runtime:
 INT4 Paged KV Cache", section 3), so no fp16 operand can overflow whatever the
 scales; the score factor softmax_scale * M_h stays in fp32.  These cases put
 per-channel scales log-uniformly over [2^-60, 2^100] (and per-head scales at
-the same extremes), with keys drawn as codes times scales in fp32, and require
+the same extremes, and at the intermediate magnitudes where the running
+maximum's own rounding reaches whole powers of two), with keys drawn as codes
+times scales in fp32, and require
 the usual tolerance and finite outputs.  Value scales stay ordinary so that the
 outputs fit the query dtype.
 """
@@ -28,7 +30,16 @@ SIGMA = {"int8": 40.0, "int4": 2.0, "fp8": 100.0}
 def _scales(rng, hkv, D, mode):
     if mode == "channel":
         return np.exp2(rng.uniform(-60.0, 100.0, (hkv, D))).astype(np.float32)
+    if mode == "mid":
+        # maxima of the log2 scores between ~2^22 and ~2^40: where an fp32
+        # running maximum has an ulp of 1 to 2^17, so the exponent of an fp16
+        # P must be formed from exact differences to it
+        return np.array([2.0 ** 14, 2.0 ** 20, 2.0 ** 26, 2.0 ** 32][:hkv], np.float32)
     return np.array([2.0 ** 100, 2.0 ** -60, 1.0, 6e4][:hkv], np.float32)
+
+
+def _scale_mode(mode):
+    return "channel" if mode == "channel" else "head"
 
 
 def _near_ties(w, kc, vc, rel=2.0 ** -17):
@@ -83,7 +94,7 @@ def _run(w, splits=None):
 
 @pytest.mark.parametrize("fmt", ["int8", "int4", "fp8"])
 @pytest.mark.parametrize("qdt", ["f16", "bf16", "f32"])
-@pytest.mark.parametrize("mode", ["channel", "head"])
+@pytest.mark.parametrize("mode", ["channel", "head", "mid"])
 @pytest.mark.parametrize("splits", [1, 4])
 def test_decode_extreme_key_scales(fmt, qdt, mode, splits):
     name = "ext_dec_%s_%s_%s_s%d" % (fmt, qdt, mode, splits)
@@ -92,21 +103,21 @@ def test_decode_extreme_key_scales(fmt, qdt, mode, splits):
     w = workloads.custom(name, 41, batch=3, num_heads=16, kv_num_heads=4, head_size=128,
                          block_size=16, past=np.array([90, 0, 33]),
                          q_lens=np.ones(3, np.int32), q_dtype=qdt, kv_format=fmt,
-                         scale_mode=mode, kv_in_dtype="f32", num_splits=splits,
+                         scale_mode=_scale_mode(mode), kv_in_dtype="f32", num_splits=splits,
                          key_scale=_scales(rng, 4, 128, mode), key_code_sigma=SIGMA[fmt])
     _run(w)
 
 
 @pytest.mark.parametrize("fmt", ["int8", "int4", "fp8"])
 @pytest.mark.parametrize("qdt", ["f16", "bf16"])
-@pytest.mark.parametrize("mode", ["channel", "head"])
+@pytest.mark.parametrize("mode", ["channel", "head", "mid"])
 def test_prefill_extreme_key_scales(fmt, qdt, mode):
     name = "ext_pf_%s_%s_%s" % (fmt, qdt, mode)
     print("case", name, flush=True)
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     w = workloads.custom(name, 43, batch=3, num_heads=16, kv_num_heads=4, head_size=128,
                          block_size=16, past=np.array([0, 40, 7]), q_lens=np.array([70, 9, 0]),
-                         q_dtype=qdt, kv_format=fmt, scale_mode=mode, kv_in_dtype="f32",
+                         q_dtype=qdt, kv_format=fmt, scale_mode=_scale_mode(mode), kv_in_dtype="f32",
                          kind="prefill", key_scale=_scales(rng, 4, 128, mode),
                          key_code_sigma=SIGMA[fmt])
     _run(w)
