@@ -73,16 +73,14 @@ template <int KVF, int D, int NT = 256> struct PfGeo {
   static constexpr int C = (KVF == KV_INT4) ? D / 2 : D;     // bytes per cache row
   static constexpr int CPU = (KVF == KV_INT4) ? 32 : 16;     // channels per 16-byte unit
   static constexpr int UPR = C / 16;                         // 16-byte units per row
-  static constexpr int KUNITS = kBN * UPR;                   // K units per tile
-  static constexpr int KU_PER_T = (KUNITS + NT - 1) / NT;   // per thread
-  static constexpr int VUNITS = (kBN / 2) * UPR;             // V units (key pairs)
-  static constexpr int VU_PER_T = (VUNITS + NT - 1) / NT;
-  // LDS rows are padded by 16 bytes: 16 lanes reading the same 16-byte column
-  // of 16 consecutive rows then hit 16 different 4-bank groups, and every
-  // address is a per-lane base plus an immediate offset
+  // LDS rows: K rows are padded by 16 bytes, so 16 lanes reading the same
+  // 16-byte column of 16 consecutive rows hit 16 different 4-bank groups; V
+  // rows by 64 bytes, so the 32 lanes of a transposing 8-byte operand read
+  // (4 rows x 8 blocks of 4 channels) hit 64 different banks.  Every address
+  // is a per-lane base plus an immediate offset.
   static constexpr int KROW = D * 2 + 16;                    // bytes of a K row in LDS
-  static constexpr int VROW = kBN * 2 + 16;                  // bytes of a V^T row in LDS
-  static constexpr int TILE = kBN * KROW + D * VROW;         // one LDS buffer
+  static constexpr int VROW = D * 2 + 64;                    // bytes of a V row in LDS
+  static constexpr int TILE = kBN * KROW + kBN * VROW;       // one LDS buffer
 };
 
 // 16 raw code bytes -> 16 (or 32 for INT4) channel values, as 16-bit words of
@@ -169,15 +167,6 @@ __device__ __forceinline__ int32_t choose(bool c, int32_t a, int32_t b) {
   return b ^ ((a ^ b) & -(int32_t)c);
 }
 
-// Position of key k (0..63) of a tile inside a V^T row: within each 16-key
-// chunk c, slot 8*eta + j holds key 16c + 8(j/4) + 4*eta + j%4.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int c = k >> 4, k16 = k & 15;
-  const int eta = (k16 >> 2) & 1;
-  const int j = 4 * (k16 >> 3) + (k16 & 3);
-  return 16 * c + 8 * eta + j;
-}
-
 template <int D, int KVF, int SM, typename TQ, typename TK, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
@@ -232,7 +221,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // past kv_end read whatever the block holds there: their scores are masked
   // and their value codes are zeroed before conversion.
   static_assert(kBN == 16 * kPfWaves, "each wave stages 16 keys of a tile");
-  static_assert(Geo::VU_PER_T == 1, "one key pair x 16-byte unit of V per thread");
   const int nbt = (kBN >> lbs) > 0 ? (kBN >> lbs) : 1;       // blocks per tile (<= 4)
   const int last_blk = (kv_end - 1) >> lbs;
   const uint32_t blk_bytes = (uint32_t)bs * row_stride;
@@ -246,12 +234,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
                       table[min(first + min(2, nbt - 1), last_blk)],
                       table[min(first + min(3, nbt - 1), last_blk)]};
   };
-  // K: wave w stages keys [16w, 16w + 16) of a tile, which lie in one block
-  // for every supported block size: the block is wave-uniform and a lane's
-  // offset into it is constant.  KL loads per lane, KPL keys per load, lane l
-  // taking key l % KPL and 16-byte unit l / KPL of it: the row writes of such
-  // a load to LDS are free of bank conflicts (with the unit index running
-  // fastest over the lanes they are not).
+  // K and V alike: wave w stages keys [16w, 16w + 16) of a tile, which lie in
+  // one block for every supported block size: the block is wave-uniform and
+  // a lane's offset into it is constant.  KL loads per lane, KPL keys per
+  // load, lane l taking key l % KPL and 16-byte unit l / KPL of it: the row
+  // writes of such a load to LDS are free of bank conflicts (with the unit
+  // index running fastest over the lanes they are not).
   constexpr int KL = Geo::UPR >= 4 ? Geo::UPR / 4 : 1;
   constexpr int KPL = Geo::UPR >= 4 ? 64 / Geo::UPR : 16;      // keys per load
   const bool k_active = Geo::UPR >= 4 || lane < 16 * Geo::UPR;
@@ -259,25 +247,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   uint32_t koff[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) koff[i] = (uint32_t)(i * KPL + kx) * row_stride + 16 * kc;
-  auto k_base = [&](const TileBlocks& tb, int kt) -> const uint8_t* {
+  auto row_base = [&](const uint8_t* base, const TileBlocks& tb, int kt) -> const uint8_t* {
     const int key = kt * kBN + 16 * wave;
     const int j = (key >> lbs) - ((kt * kBN) >> lbs);         // 0..3, uniform
     const int32_t blk =
         choose(j >= 3, tb.b3, choose(j >= 2, tb.b2, choose(j >= 1, tb.b1, tb.b0)));
-    return kbase + ((size_t)blk * bs + (key & (bs - 1))) * row_stride;
-  };
-  // V: thread t stages keys 2m, 2m+1 (m = t % 32) of 16-byte unit t / 32; the
-  // 32 key pairs of a wave span the whole tile, so the block is chosen per lane
-  // from the tile's (at most 4) blocks.
-  const int vm = tid % (kBN / 2), vc = tid / (kBN / 2);
-  const bool v_active = Geo::VUNITS % kPfThreads == 0 || tid < Geo::VUNITS;
-  const int vj = bs <= kBN ? (2 * vm) >> lbs : 0;
-  const uint32_t voff = (uint32_t)(bs <= kBN ? (2 * vm) & (bs - 1) : 2 * vm) * row_stride + 16 * vc;
-  auto v_addr = [&](const TileBlocks& tb, int kt) -> const uint8_t* {
-    const int r0 = bs > kBN ? (kt * kBN) & (bs - 1) : 0;      // tile's first row in its block
-    const int32_t blk =
-        choose(vj >= 3, tb.b3, choose(vj >= 2, tb.b2, choose(vj >= 1, tb.b1, tb.b0)));
-    return vbase + (size_t)r0 * row_stride + (size_t)(uint32_t)blk * blk_bytes + voff;
+    return base + ((size_t)blk * bs + (key & (bs - 1))) * row_stride;
   };
   // Raw codes of a tile, held by this thread between their load and their
   // conversion into LDS one step later (K codes of tile t+3 and V codes of
@@ -286,80 +261,64 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // to MFMA accumulators and then drain the loads to avoid overwriting a
   // vector-memory source operand.
   struct RawK { u32x4 k[KL]; };
-  struct RawV { u32x4 v[2]; const uint8_t* va; int kt; };
   auto load_k = [&](RawK& r, const TileBlocks& tb, int kt) {
-    const uint8_t* kb = k_base(tb, kt);
+    const uint8_t* rb = row_base(kbase, tb, kt);
     if (k_active) {
 #pragma unroll
-      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(rb + koff[i]);
     }
   };
-  auto load_v = [&](RawV& r, const TileBlocks& tb, int kt) {
-    r.kt = kt;
-    r.va = v_addr(tb, kt);
-    if (v_active) {
-      r.v[0] = *reinterpret_cast<const u32x4*>(r.va);
-      r.v[1] = *reinterpret_cast<const u32x4*>(r.va + row_stride);
+  auto load_v = [&](RawK& r, const TileBlocks& tb, int kt) {
+    const uint8_t* rb = row_base(vbase, tb, kt);
+    if (k_active) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(rb + koff[i]);
     }
   };
-  // Conversions into LDS buffer `buf`: the K rows of a tile (row-major) and
-  // its V^T rows (channel-major, keys in the PV operand order), in pieces that
-  // phase B spreads over its matrix products.
-  auto stage_k_unit = [&](const RawK& r, int buf, int i) {   // K unit i of this lane
+  // Conversions into LDS buffer `buf`: the K and V rows of a tile, row-major,
+  // in pieces that phase B spreads over its matrix products.
+  typedef uint32_t KWords[Geo::CPU / 2];
+  auto stage_write = [&](int buf, int vpart, int i, const KWords& w) {   // unit i of this lane
     if (!k_active) return;
-    uint8_t* kl = lds[buf] + (16 * wave) * Geo::KROW;
-    const int k = i * KPL + kx, c = kc;
-    uint32_t w[Geo::CPU / 2];
-    decode_unit<KVF, TK>(r.k[i], w);
-    // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
+    const int rowb = vpart ? Geo::VROW : Geo::KROW;
+    uint8_t* rl = lds[buf] + (vpart ? kBN * Geo::KROW : 0) + (16 * wave + i * KPL + kx) * rowb;
+    // channels [CPU*kc, CPU*kc + CPU) = 16-byte chunks CPU*kc/8 ...
 #pragma unroll
     for (int j = 0; j < Geo::CPU / 8; ++j)
-      *reinterpret_cast<u32x4*>(kl + k * Geo::KROW + 2 * Geo::CPU * c + 16 * j) =
+      *reinterpret_cast<u32x4*>(rl + 2 * Geo::CPU * kc + 16 * j) =
           (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
   };
-  typedef uint32_t VWords[Geo::CPU / 2];
-  auto stage_v_decode = [&](const RawV& r, VWords& w0, VWords& w1) {
-    asm volatile("" ::"v"(r.va));
-    u32x4 v0 = r.v[0], v1 = r.v[1];
+  // V codes of unit i of tile t as fp16
+  auto v_decode = [&](const RawK& r, int t, int i, KWords& w) {
+    u32x4 v = r.k[i];
     if constexpr (KVF == KV_FP8) {
       // keys past kv_end hold whatever their block holds: E4M3 NaN codes
       // there would survive the zero P (0 * NaN), so they become zeros
-      const int key = r.kt * kBN + 2 * vm;
-      v0 &= (u32x4)(key < kv_end ? ~0u : 0u);
-      v1 &= (u32x4)(key + 1 < kv_end ? ~0u : 0u);
+      v &= (u32x4)(t * kBN + 16 * wave + i * KPL + kx < kv_end ? ~0u : 0u);
     }
-    decode_unit<KVF, f16>(v0, w0);
-    decode_unit<KVF, f16>(v1, w1);
-  };
-  // V^T rows of channels CPU*vc + [j0, j1): consecutive lanes take consecutive
-  // key pairs of one 16-byte unit, so the 32 lanes of a write hit 32 banks
-  auto stage_v_write = [&](int buf, const VWords& w0, const VWords& w1, int j0, int j1) {
-    if (!v_active) return;
-    uint8_t* vl = lds[buf] + kBN * Geo::KROW;
-    const int pos = vt_pos(2 * vm);                        // even: keys 2m, 2m+1 adjacent
-#pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      const int d = Geo::CPU * vc + j;
-      // {key 2m, key 2m+1} of channel d: the matching halves of w0, w1
-      const uint32_t pair = perm(w1[j >> 1], w0[j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
-      *reinterpret_cast<uint32_t*>(vl + d * Geo::VROW + 2 * pos) = pair;
-    }
+    decode_unit<KVF, f16>(v, w);
   };
   auto store_k = [&](const RawK& r, int buf) {
 #pragma unroll
-    for (int i = 0; i < KL; ++i) stage_k_unit(r, buf, i);
+    for (int i = 0; i < KL; ++i) {
+      KWords w;
+      decode_unit<KVF, TK>(r.k[i], w);
+      stage_write(buf, 0, i, w);
+    }
   };
-  auto store_v = [&](const RawV& r, int buf) {
-    VWords w0, w1;
-    stage_v_decode(r, w0, w1);
-    stage_v_write(buf, w0, w1, 0, Geo::CPU);
+  auto store_v = [&](const RawK& r, int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      KWords w;
+      v_decode(r, t, i, w);
+      stage_write(buf, 1, i, w);
+    }
   };
 
   // tiles 0 and 1 are converted before the first step; tile 2's K codes and
   // tile 1's V codes are in registers when it starts
   TileBlocks tbA = tile_blocks(0), tbB = tile_blocks(1);
-  RawK rk, rk1;
-  RawV rv;
+  RawK rk, rk1, rv;
   load_k(rk, tbA, 0);
   load_v(rv, tbA, 0);
   load_k(rk1, tbB, 1);
@@ -496,6 +455,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4 && i < NM; ++i) ka[i] = *reinterpret_cast<const kvec*>(kaddr(i));
     }
+    // score pair j = scores 2j, 2j+1 of this lane (block j/8, registers
+    // 2j%16, +1); bundle i forms the exponent of pair i+1, the powers of pair
+    // i and the fp16 values and sums of pair i-1, so no result is used in the
+    // bundle that makes it
+    auto arg = [&](int j, int e) { return fmaf(s_cur[j >> 3][(2 * j + e) & 15], c2, bias); };
+    float x0 = arg(0, 0), x1 = arg(0, 1), y0 = 0.f, y1 = 0.f;
+    auto finish = [&](int j, float a0, float a1) {
+      const f16 e0 = (f16)a0, e1 = (f16)a1;
+      const int st = j >> 3, r = (2 * j) & 15;
+      p[2 * st + (r >> 3)][r & 7] = e0;
+      p[2 * st + (r >> 3)][(r & 7) + 1] = e1;
+      lp[j & 3] = __builtin_amdgcn_fdot2((f16x2){e0, e1}, ones, lp[j & 3], false);
+    };
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -505,14 +477,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
           if (i + 4 < NM) ka[i & 3] = *reinterpret_cast<const kvec*>(kaddr(i + 4));
         }
       }
-      // scores 2i, 2i+1 of this lane: block st, registers r, r+1
-      const int st = i >> 3, r = (2 * i) & 15;
-      const f16 e0 = (f16)fast_exp2(fmaf(s_cur[st][r], c2, bias));
-      const f16 e1 = (f16)fast_exp2(fmaf(s_cur[st][r + 1], c2, bias));
-      p[2 * st + (r >> 3)][r & 7] = e0;
-      p[2 * st + (r >> 3)][(r & 7) + 1] = e1;
-      lp[i & 3] = __builtin_amdgcn_fdot2((f16x2){e0, e1}, ones, lp[i & 3], false);
+      if (i > 0) finish(i - 1, y0, y1);
+      y0 = fast_exp2(x0);
+      y1 = fast_exp2(x1);
+      if (i + 1 < 16) {
+        x0 = arg(i + 1, 0);
+        x1 = arg(i + 1, 1);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    finish(15, y0, y1);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Phase B of step t: O^T += V^T P^T for tile t (product i: channel tile
@@ -520,27 +494,45 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // (into buffer t & 1) and the V codes of tile t+1 (into buffer (t+1) & 1),
   // and then the loads of the codes of K(t+3) and V(t+2) into the same
   // registers.
-  auto phase_b = [&](int t, const f16x8 (&p)[4], RawK& rk, RawV& rv, const TileBlocks& tbk,
+  // The V^T operand comes from the row-major V tile through transposing
+  // reads (ds_read_b64_tr_b16): in each 16-lane group, lane s gives the
+  // address of 4 channels (block s%4 of the group's 16) of one key (s/4 of a
+  // run of 4), and lane j receives channel j of those 4 keys.  Two reads give
+  // a lane the 8 keys its operand slots hold in the layout of P (keys
+  // 16c + 4*eta + {0..3, 8..11} of chunk c).
+  const int vg = lane >> 4, vs = lane & 15;
+  const uint32_t v_lane = (uint32_t)((4 * (vg >> 1) + (vs >> 2)) * Geo::VROW +
+                                     2 * (16 * (vg & 1) + 4 * (vs & 3)));
+  auto phase_b = [&](int t, const f16x8 (&p)[4], RawK& rk, RawK& rv, const TileBlocks& tbk,
                      const TileBlocks& tbv) {
     constexpr int NM = 4 * NDT;                     // products (16 for D = 128)
-    constexpr int VW = Geo::CPU / 8;                // V^T channels written per bundle
-    const uint8_t* vp = lds[t & 1] + kBN * Geo::KROW + n * Geo::VROW + 16 * eta;
-    auto vaddr = [&](int i) { return vp + 32 * (i >> 2) * Geo::VROW + 32 * (i & 3); };
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint8_t* vb = lds[t & 1] + kBN * Geo::KROW + v_lane;
+    auto vread = [&](int i) -> f16x8 {
+      const uint8_t* q = vb + 16 * (i & 3) * Geo::VROW + 64 * (i >> 2);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 8 * Geo::VROW));
+      return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     f16x8 va[4];
-    VWords w0, w1;
+    KWords kw[2], vw[2];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) va[i] = *reinterpret_cast<const f16x8*>(vaddr(i));
+    for (int i = 0; i < 4; ++i) va[i] = vread(i);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i < NM) {
         o[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i & 3], p[i & 3], o[i >> 2], 0, 0, 0);
-        if (i + 4 < NM) va[i & 3] = *reinterpret_cast<const f16x8*>(vaddr(i + 4));
+        if (i + 4 < NM) va[i & 3] = vread(i + 4);
       }
-      if (i < KL) stage_k_unit(rk, t & 1, i);
-      if (i == KL) stage_v_decode(rv, w0, w1);
-      if (i > KL && i <= KL + 8) stage_v_write((t + 1) & 1, w0, w1, VW * (i - KL - 1), VW * (i - KL));
+      // unit u: K decoded in bundle u and written in bundle u+1, V decoded in
+      // bundle KL+1+u and written in bundle KL+2+u
+      if (i >= 1 && i <= KL) stage_write(t & 1, 0, i - 1, kw[(i - 1) & 1]);
+      if (i < KL) decode_unit<KVF, TK>(rk.k[i], kw[i & 1]);
+      if (i >= KL + 2 && i <= 2 * KL + 1) stage_write((t + 1) & 1, 1, i - KL - 2, vw[(i - KL - 2) & 1]);
+      if (i >= KL + 1 && i <= 2 * KL) v_decode(rv, t + 1, i - KL - 1, vw[(i - KL - 1) & 1]);
       if (i == 15) {
         load_k(rk, tbk, t + 3);
         load_v(rv, tbv, t + 2);
@@ -572,7 +564,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   };
 
   store_k(rk, 0);
-  store_v(rv, 0);
+  store_v(rv, 0, 0);
   store_k(rk1, 1);
   load_k(rk, tb2, 2);
   load_v(rv, tbB, 1);
