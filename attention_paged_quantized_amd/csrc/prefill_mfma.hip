@@ -244,9 +244,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   constexpr int KPL = Geo::UPR >= 4 ? 64 / Geo::UPR : 16;      // keys per load
   const bool k_active = Geo::UPR >= 4 || lane < 16 * Geo::UPR;
   const int kx = lane % KPL, kc = lane / KPL;                  // key, unit
-  uint32_t koff[KL];
+  // (V rows are 320 bytes apart for D = 128, where rows kx and kx+4 share
+  // banks: the second four rows of a load take their units in swapped pairs)
+  const int vc = kc ^ ((kx >> 2) & 1);
+  uint32_t koff[KL], voff[KL];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) koff[i] = (uint32_t)(i * KPL + kx) * row_stride + 16 * kc;
+  for (int i = 0; i < KL; ++i) {
+    koff[i] = (uint32_t)(i * KPL + kx) * row_stride + 16 * kc;
+    voff[i] = (uint32_t)(i * KPL + kx) * row_stride + 16 * vc;
+  }
   auto row_base = [&](const uint8_t* base, const TileBlocks& tb, int kt) -> const uint8_t* {
     const int key = kt * kBN + 16 * wave;
     const int j = (key >> lbs) - ((kt * kBN) >> lbs);         // 0..3, uniform
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     const uint8_t* rb = row_base(vbase, tb, kt);
     if (k_active) {
 #pragma unroll
-      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(rb + koff[i]);
+      for (int i = 0; i < KL; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(rb + voff[i]);
     }
   };
   // Conversions into LDS buffer `buf`: the K and V rows of a tile, row-major,
@@ -281,11 +287,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   auto stage_write = [&](int buf, int vpart, int i, const KWords& w) {   // unit i of this lane
     if (!k_active) return;
     const int rowb = vpart ? Geo::VROW : Geo::KROW;
+    const int c = vpart ? vc : kc;
     uint8_t* rl = lds[buf] + (vpart ? kBN * Geo::KROW : 0) + (16 * wave + i * KPL + kx) * rowb;
-    // channels [CPU*kc, CPU*kc + CPU) = 16-byte chunks CPU*kc/8 ...
+    // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
 #pragma unroll
     for (int j = 0; j < Geo::CPU / 8; ++j)
-      *reinterpret_cast<u32x4*>(rl + 2 * Geo::CPU * kc + 16 * j) =
+      *reinterpret_cast<u32x4*>(rl + 2 * Geo::CPU * c + 16 * j) =
           (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
   };
   // V codes of unit i of tile t as fp16
