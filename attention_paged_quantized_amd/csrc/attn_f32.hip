@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int kv_len = past + qlen;
   const int visible = past + i + 1;                    // keys 0..past+i
   const int nb = (kv_len + bs - 1) / bs;
-  const int S = a.num_splits;
+  const int S = a.num_splits;                 // one partial per chunk (part_count == S)
   const int kbeg = (int)(((long)chunk * nb) / S) * bs;
   const int kend = min(visible, (int)(((long)(chunk + 1) * nb) / S) * bs);
   const int32_t* table = a.block_table + (size_t)b * a.max_blocks;

@@ -90,7 +90,7 @@ static int launch_combine_d(const AttnArgs& a, hipStream_t st) {
   case DTV:                                                                                 \
     hipLaunchKernelGGL((combine_kernel<TYPE, D>), grid, dim3(kCombineThreads), 0, st, a.part_o, \
                        a.part_lse, (TYPE*)a.out, a.v_scale, a.num_heads, a.num_heads / a.hkv,   \
-                       a.scale_mode == SCALE_CHANNEL ? 1 : 0, a.num_splits);                  \
+                       a.scale_mode == SCALE_CHANNEL ? 1 : 0, a.part_count);                  \
     return 0;
     PAQ_COMBINE_CASE(DT_F32, float)
     PAQ_COMBINE_CASE(DT_F16, f16)
@@ -101,7 +101,7 @@ static int launch_combine_d(const AttnArgs& a, hipStream_t st) {
 }
 
 int launch_combine(const AttnArgs& a, hipStream_t st) {
-  if (a.num_splits > kCombineMaxSplits || a.token_count == 0) return -1;
+  if (a.part_count > kCombineMaxSplits || a.token_count == 0) return -1;
   if (a.head_size == 128) return launch_combine_d<128>(a, st);
   if (a.head_size == 64) return launch_combine_d<64>(a, st);
   return -1;

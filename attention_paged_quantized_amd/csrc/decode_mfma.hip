@@ -5,7 +5,8 @@
 // heads (HW = 128 / row bytes, so every copied row segment is a whole 128-byte
 // line) with its own online softmax.  Single pass: the 8 waves of a
 // workgroup share one (sequence, head group) and merge through LDS at the end;
-// split-KV: each wave owns one chunk and writes partials for the combine.
+// split-KV: each wave owns one chunk, and the workgroup merges its chunks
+// through LDS and writes one partial for the combine.
 // Decode is HBM-bound (every K/V byte is read once -- "GQA GEMV decode",
 // why-it-is-good item 1), so the design streams the raw codes HBM -> LDS with
 // whole-line non-temporal DMA copies, reads each lane's operand bytes from
@@ -31,8 +32,9 @@
 //   exceeds it by more than 2^8 are the maxima exchanged and the accumulators
 //   rescaled, so P stays <= 2^15, inside fp16 range.
 // * Split-KV ("flash decoding", "GQA GEMV decode" section 2): chunk c covers
-//   blocks [c*nb/S, (c+1)*nb/S) of the sequence and writes the normalised
-//   partial output and its log-sum-exp for the combine kernel.
+//   blocks [c*nb/S, (c+1)*nb/S) of the sequence; each workgroup writes the
+//   normalised partial output of its chunks and its log-sum-exp for the
+//   combine kernel.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -495,10 +497,11 @@ __device__ __forceinline__ void chunk_keys(int c, int nb, int S, int bs, int kv_
 //    tiles of the whole sequence in turn, each with its own online softmax,
 //    and merge through LDS at the end.
 //  * Split-KV (SPLIT true): wave w of workgroup z takes chunk z * NW + w
-//    (blocks [c*nb/S, (c+1)*nb/S), "GQA GEMV decode", section 2) and writes the
-//    chunk's partial output -- normalised, value scale not yet applied; the
-//    combine applies it once -- and its log-sum-exp.  The waves never
-//    synchronise.
+//    (blocks [c*nb/S, (c+1)*nb/S), "GQA GEMV decode", section 2).  The waves
+//    never wait for each other while streaming; at the end they merge their
+//    chunks through LDS as in single pass, and the workgroup writes one
+//    partial output for its NW chunks -- normalised, value scale not yet
+//    applied; the combine applies it once -- and its log-sum-exp.
 template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
@@ -524,9 +527,12 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
   int kb, ke, stride, chunk = 0;
   if constexpr (SPLIT) {
     chunk = blockIdx.z * NW + wave;
-    if (chunk >= a.num_splits) return;                    // no workgroup barrier in split mode
     const int nb = (kv_len + a.block_size - 1) >> lbs;
-    chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
+    if (chunk < a.num_splits) {
+      chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
+    } else {
+      kb = ke = 0;                                        // past the last chunk: empty
+    }
     stride = 32;
   } else {
     kb = 32 * wave;
@@ -591,62 +597,46 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
   wait_vmcnt_le<0>();
   __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (SPLIT) {
-    // partial output (value scale not applied) and log-sum-exp of the chunk
-    const int S = a.num_splits;
+  // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
+  __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];        // running max, sum per wave
+  float* wo = reinterpret_cast<float*>(myring);            // [HW][kDecMaxGroup][D] per wave
+  static_assert(HW * kDecMaxGroup * D * 4 <= NS * SG::SLOT, "merge area");
 #pragma unroll
-    for (int hh = 0; hh < HW; ++hh) {
-      const float L = rows_sum(st[hh].l);
-      if (col < G) {
-        const int hq = (blockIdx.x * HW + hh) * G + col;
-        const size_t pi = ((size_t)q0 * H + hq) * S + chunk;
-        const float inv = (L > 0.f) ? 1.f / L : 0.f;      // both carry 2^7
-        float* po = a.part_o + pi * D;
+  for (int hh = 0; hh < HW; ++hh) {
+    const float l_run = rows_sum(st[hh].l);
+    if (col < G) {
+      if (grp == 0) { sm_ml[wave][hh][0][col] = st[hh].m; sm_ml[wave][hh][1][col] = l_run; }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d0 = (D / 16) * (4 * grp + r);
+      for (int nbk = 0; nbk < NPV; ++nbk)
 #pragma unroll
-          for (int nbk = 0; nbk < NPV; ++nbk)
-            po[d0 + nbk] = (L > 0.f) ? v_unbias<KVF>(st[hh].o[nbk][r] * inv, d0 + nbk) : 0.f;
-        }
-        if (grp == 0)
-          a.part_lse[pi] = (L > 0.f) ? (st[hh].m + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          wo[(hh * kDecMaxGroup + col) * D + (D / 16) * (4 * grp + r) + nbk] = st[hh].o[nbk][r];
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < HW * G * D; t += NW * 64) {
+    const int hh = t / (G * D), cq = (t / D) % G, d = t % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][hh][0][cq]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(sm_ml[w][hh][0][cq] - M);
+        L += f * sm_ml[w][hh][1][cq];
+        O += f * reinterpret_cast<const float*>(ring[w])[(hh * kDecMaxGroup + cq) * D + d];
       }
     }
-  } else {
-    // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
-    __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];      // running max, sum per wave
-    float* wo = reinterpret_cast<float*>(myring);          // [HW][kDecMaxGroup][D] per wave
-    static_assert(HW * kDecMaxGroup * D * 4 <= NS * SG::SLOT, "merge area");
-#pragma unroll
-    for (int hh = 0; hh < HW; ++hh) {
-      const float l_run = rows_sum(st[hh].l);
-      if (col < G) {
-        if (grp == 0) { sm_ml[wave][hh][0][col] = st[hh].m; sm_ml[wave][hh][1][col] = l_run; }
-#pragma unroll
-        for (int nbk = 0; nbk < NPV; ++nbk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            wo[(hh * kDecMaxGroup + col) * D + (D / 16) * (4 * grp + r) + nbk] = st[hh].o[nbk][r];
-      }
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < HW * G * D; t += NW * 64) {
-      const int hh = t / (G * D), cq = (t / D) % G, d = t % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][hh][0][cq]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float f = fast_exp2(sm_ml[w][hh][0][cq] - M);
-          L += f * sm_ml[w][hh][1][cq];
-          O += f * reinterpret_cast<const float*>(ring[w])[(hh * kDecMaxGroup + cq) * D + d];
-        }
-      }
-      const int ho = blockIdx.x * HW + hh;
-      const int hq = ho * G + cq;
+    const int ho = blockIdx.x * HW + hh;
+    const int hq = ho * G + cq;
+    if constexpr (SPLIT) {
+      // partial of this workgroup's chunks (value scale not applied) and its
+      // log-sum-exp (both O and L carry 2^7)
+      const size_t pi = ((size_t)q0 * H + hq) * a.part_count + blockIdx.z;
+      a.part_o[pi * D + d] = (L > 0.f) ? v_unbias<KVF>(O / L, d) : 0.f;
+      if (d == 0) a.part_lse[pi] = (L > 0.f) ? (M + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
+    } else {
       const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
       const float val = (L > 0.f) ? v_unbias<KVF>(O / L, d) * vs : 0.f;   // both carry 2^7
       reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);

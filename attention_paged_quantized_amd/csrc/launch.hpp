@@ -40,6 +40,7 @@ struct AttnArgs {
   int batch, token_count, num_heads, hkv, head_size, block_size, max_blocks;
   int q_dtype, kv_format, scale_mode;
   int num_splits;       // 1 = single pass (no partials)
+  int part_count;       // split-KV: partials per (row, head) in the workspace
   int max_query_len;    // exact, from the host cum_q
   int max_kv_len;       // longest sequence with new rows (host)
   int block_size_log2;  // block_size is a power of two

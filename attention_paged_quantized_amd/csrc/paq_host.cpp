@@ -188,7 +188,9 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
     p->grid_z = S;
   }
   if (S > 1) {
-    const size_t rows = (size_t)d->token_count * d->num_heads * S;
+    // one partial per (row, head) and grid slice: a workgroup of the MFMA
+    // kernel merges its chunks first, the fp32 kernel writes one per chunk
+    const size_t rows = (size_t)d->token_count * d->num_heads * p->grid_z;
     p->workspace_bytes = align_up(rows * d->head_size * sizeof(float)) + align_up(rows * sizeof(float));
   }
   return PAQ_OK;
@@ -340,7 +342,8 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
   if (p.num_splits > 1) {
     rc = device_cu_count(&a.num_cus);
     if (rc) return rc;
-    const size_t rows = (size_t)d->token_count * d->num_heads * p.num_splits;
+    a.part_count = p.grid_z;
+    const size_t rows = (size_t)d->token_count * d->num_heads * a.part_count;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
   }

@@ -159,7 +159,8 @@ size_t paged_attn_decode_workspace_size(const paq_desc* d, const int32_t* cum_q_
 /* GQA paged decode: every q_len_b must be 0 or 1.  Split-KV (path SPLIT) needs
  * `workspace` (device, 16-byte aligned) of at least
  * paged_attn_decode_workspace_size() bytes; it holds fp32 partial outputs and
- * log-sum-exps and is overwritten.  fp32 queries take the portable fp32
+ * log-sum-exps (one per output row, head and slice of plan.grid_z: a
+ * workgroup of the 16-bit kernel merges its chunks first) and is overwritten.  fp32 queries take the portable fp32
  * kernel; fp16/bf16 queries take the MFMA kernel, which folds the per-channel
  * k_scale into the query ("ONNX Runtime: INT4 Paged KV Cache", section 3).
  * Returns PAQ_ERR_WORKSPACE if the workspace is missing or too small. */

@@ -57,13 +57,14 @@ def test_plan_decode_paths_and_workspace():
     p = paq.paq_plan_decode(d, [0, 1, 2, 2], [37, 100, 0], 0, 256)
     assert (p.max_query_len, p.max_kv_len, p.active_seqs, p.work_units) == (1, 101, 2, 4)
     assert paq.PATHS[p.path] == "f32_single" or paq.PATHS[p.path] == "f32_split"
-    # long INT4 decode with 128 chunks: workspace = T*H*S*(D+1) fp32 (aligned)
+    # long INT4 decode with 128 chunks: a workgroup merges its 8 chunks, so the
+    # workspace holds T*H*(S/8)*(D+1) fp32 (aligned)
     d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
     p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 128, 256)
     # one wave per chunk and per pair of INT4 kv heads (a 128-byte line), 8 waves
     # per workgroup: grid (8 / 2, 4, 128 / 8)
     assert p.num_splits == 128 and (p.grid_x, p.grid_y, p.grid_z) == (4, 4, 16)
-    assert p.workspace_bytes == 4 * 32 * 128 * 128 * 4 + 4 * 32 * 128 * 4
+    assert p.workspace_bytes == 4 * 32 * 16 * 128 * 4 + 4 * 32 * 16 * 4
     assert paq.paged_attn_decode_workspace_size(d, _cum([1] * 4), [32768] * 4, 128) == \
         p.workspace_bytes
     # 256 (sequence, kv head) units fill 256 CUs: automatic choice is one pass
