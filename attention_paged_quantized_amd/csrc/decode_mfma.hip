@@ -228,12 +228,23 @@ template <int KVF, int D, int HW> struct WaveCopy {
   // valid row; their scores are masked).  Each 16-key half of the tile lies in
   // one physical block (block_size is a multiple of 16, and of 32 when a block
   // holds both halves).
+  struct Blocks { int32_t b0, b1; };
+  __device__ __forceinline__ static Blocks blocks(int k0, int kend, int lbs,
+                                                 const int32_t* __restrict__ table) {
+    // (clamped into [0, kend - 1]: an empty range reads entry 0, never used)
+    return Blocks{table[max(0, min(k0, kend - 1)) >> lbs], table[max(0, min(k0 + 16, kend - 1)) >> lbs]};
+  }
   __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs,
                                         const int32_t* __restrict__ table, const uint8_t* kbase,
                                         const uint8_t* vbase, uint32_t row_stride) const {
+    issue(slot, k0, kend, lbs, blocks(k0, kend, lbs, table), kbase, vbase, row_stride);
+  }
+  __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs, Blocks bb,
+                                        const uint8_t* kbase, const uint8_t* vbase,
+                                        uint32_t row_stride) const {
     const int bmask = (1 << lbs) - 1;
-    const size_t blk0 = (size_t)table[min(k0, kend - 1) >> lbs] << lbs;
-    const size_t blk1 = (size_t)table[min(k0 + 16, kend - 1) >> lbs] << lbs;
+    const size_t blk0 = (size_t)bb.b0 << lbs;
+    const size_t blk1 = (size_t)bb.b1 << lbs;
     // key k0 + r sits in row (k0 & bmask) + r of block blk0 for r < 16 and in
     // row ((k0 + 16) & bmask) + r - 16 of block blk1 otherwise
     const size_t base0 = (blk0 + (size_t)(k0 & bmask)) * row_stride;
@@ -573,6 +584,9 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
 #pragma unroll
     for (int i = 0; i < NPV; ++i) st[hh].o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   int cur = 0;
+  // block ids of the next tile to issue, fetched one iteration ahead
+  typename WaveCopy<KVF, D, HW>::Blocks nb_next =
+      WaveCopy<KVF, D, HW>::blocks(kb + NS * stride, ke, lbs, table);
   for (int k = kb; k < ke; k += stride) {
     // this tile's copies are done once at most the later tiles' remain
     __builtin_amdgcn_sched_barrier(0);
@@ -586,8 +600,9 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
     const int kn = k + NS * stride;
-    if (kn < ke) cp.issue(slot, kn, ke, lbs, table, kbase, vbase, row_stride);
+    if (kn < ke) cp.issue(slot, kn, ke, lbs, nb_next, kbase, vbase, row_stride);
     else wait_vmcnt_le<0>();                              // nothing more to issue: keep vmcnt exact
+    nb_next = WaveCopy<KVF, D, HW>::blocks(kn + stride, ke, lbs, table);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hh = 0; hh < HW; ++hh)
