@@ -162,6 +162,35 @@ __device__ __forceinline__ void decode_unit<KV_INT4, bf16>(const u32x4& w, uint3
     }
 }
 
+// 16 raw value codes -> the PV operand: the exact fp16 values for FP8, and
+// for the integer formats their affine images 1152 + v (INT8) and 1032 + v
+// (INT4), the 0x6400 constructions without their bias subtraction.  The
+// epilogue removes the bias once: O/l - bias, with l the sum of the same fp16
+// probabilities the products use.
+template <int KVF> constexpr float kPfVBias = KVF == KV_INT8 ? 1152.f : KVF == KV_INT4 ? 1032.f : 0.f;
+template <int KVF>
+__device__ __forceinline__ void decode_unit_v(const u32x4& w, uint32_t (&out)[PfGeo<KVF, 128>::CPU / 2]) {
+  if constexpr (KVF == KV_INT8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = w[i] ^ 0x80808080u;
+      out[2 * i] = perm(0x64646464u, x, 0x04010400u);
+      out[2 * i + 1] = perm(0x64646464u, x, 0x04030402u);
+    }
+  } else if constexpr (KVF == KV_INT4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = w[i] ^ 0x88888888u;
+      out[4 * i] = ((x & 0xFu) | ((x << 12) & 0xF0000u)) | 0x64006400u;
+      out[4 * i + 1] = (((x >> 8) & 0xFu) | ((x << 4) & 0xF0000u)) | 0x64006400u;
+      out[4 * i + 2] = (((x >> 16) & 0xFu) | ((x >> 4) & 0xF0000u)) | 0x64006400u;
+      out[4 * i + 3] = (((x >> 24) & 0xFu) | ((x >> 12) & 0xF0000u)) | 0x64006400u;
+    }
+  } else {
+    decode_unit<KVF, f16>(w, out);
+  }
+}
+
 // a if c else b, computed on the values
 __device__ __forceinline__ int32_t choose(bool c, int32_t a, int32_t b) {
   return b ^ ((a ^ b) & -(int32_t)c);
@@ -295,15 +324,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       *reinterpret_cast<u32x4*>(rl + 2 * Geo::CPU * c + 16 * j) =
           (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
   };
-  // V codes of unit i of tile t as fp16
-  auto v_decode = [&](const RawK& r, int t, int i, KWords& w) {
-    u32x4 v = r.k[i];
+  // V codes of unit i of tile t as the PV operand
+  auto v_decode = [&](const RawK& r, int t, int i, KWords& w) { decode_unit_v<KVF>(r.k[i], w); };
+  // Keys past kv_end hold whatever their block holds: E4M3 NaN codes there
+  // would survive the zero P (0 * NaN).  For FP8, once the V rows of a tile
+  // that reaches past kv_end are written, this lane's rows of such keys are
+  // overwritten with zeros (same lane, same addresses: the writes stay in
+  // order).
+  auto v_zero_tail = [&](int t, int buf) {
     if constexpr (KVF == KV_FP8) {
-      // keys past kv_end hold whatever their block holds: E4M3 NaN codes
-      // there would survive the zero P (0 * NaN), so they become zeros
-      v &= (u32x4)(t * kBN + 16 * wave + i * KPL + kx < kv_end ? ~0u : 0u);
+      if ((t + 1) * kBN > kv_end) {
+        const KWords z = {};
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+          if (t * kBN + 16 * wave + i * KPL + kx >= kv_end) stage_write(buf, 1, i, z);
+      }
     }
-    decode_unit<KVF, f16>(v, w);
   };
   auto store_k = [&](const RawK& r, int buf) {
 #pragma unroll
@@ -320,6 +356,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       v_decode(r, t, i, w);
       stage_write(buf, 1, i, w);
     }
+    v_zero_tail(t, buf);
   };
 
   // tiles 0 and 1 are converted before the first step; tile 2's K codes and
@@ -565,6 +602,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       exps(s_cur, p, lp, true);
     l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     phase_b(t, p, rk, rv, tbB, tbA);
+    v_zero_tail(t + 1, (t + 1) & 1);
     __syncthreads();
     tbA = tbB;
     tbB = tbC;
@@ -592,6 +630,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int tok = tok0 + wave * TPW + n / G;
   if (tok < qlen) {
     const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;       // both carry 2^7
+    const float bias = (l_run > 0.f) ? kPfVBias<KVF> : 0.f;
     TQ* orow = reinterpret_cast<TQ*>(a.out) + ((size_t)(q0 + tok) * H + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -599,7 +638,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * dt + 8 * (r >> 2) + 4 * eta + (r & 3);
         const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[h * D + d] : a.v_scale[h];
-        orow[d] = from_f32<TQ>(o[dt][r] * inv * vs);
+        orow[d] = from_f32<TQ>((o[dt][r] * inv - bias) * vs);
       }
   }
 }
