@@ -5,10 +5,12 @@
 // are sums of probability-weighted value codes; the per-channel (or per-head)
 // value scale, the same for every chunk, is applied here once.
 //
-// One workgroup of 4 waves per (row, head): the waves take every 4th chunk,
-// each lane owns D/64 consecutive channels (one vector load per chunk), and
-// the four partial sums meet in LDS.  The loads of a wave are independent, so
-// many are in flight at once.
+// One workgroup of 4 waves per (row, head).  The waves take every 4th chunk,
+// four chunks per round: each lane loads their log-sum-exps and its D/64
+// consecutive channels of their partials together, so one memory round trip
+// serves the whole merge.  Each wave keeps a running maximum and rescales its
+// sums when it grows (the merge is exact in any order up to rounding); the
+// four wave results meet in LDS.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -27,55 +29,75 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int h = blockIdx.x % num_heads;
   const size_t base = ((size_t)r * num_heads + h) * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ float red[kCombineWaves];
+  __shared__ float red_m[kCombineWaves], red_w[kCombineWaves];
   __shared__ float acc_sh[kCombineWaves][D];
-  // global maximum of the chunk log-sum-exps
-  float mx = -INFINITY;
-  for (int c = tid; c < S; c += kCombineThreads) mx = fmaxf(mx, part_lse[base + c]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int i = 1; i < kCombineWaves; ++i) mx = fmaxf(mx, red[i]);
-  // weighted sum of the partial outputs; weights sum to 1 after division
+  constexpr int U = 4;                              // chunks per round and wave
+  float m = -INFINITY, wsum = 0.f;
   float acc[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll 4
-    for (int c = wave; c < S; c += kCombineWaves) {
-      const float l = part_lse[base + c];
-      const float w = (l == -INFINITY) ? 0.f : __expf(l - mx);
-      wsum += w;
-      const float* po = part_o + (base + c) * D + PER_LANE * lane;
-      if constexpr (PER_LANE == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(po);
-        acc[0] = fmaf(w, v.x, acc[0]);
-        acc[1] = fmaf(w, v.y, acc[1]);
-      } else {
-        acc[0] = fmaf(w, po[0], acc[0]);
+  for (int c0 = wave; c0 < S; c0 += U * kCombineWaves) {
+    float l[U], v[U][PER_LANE];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int c = c0 + j * kCombineWaves;
+      l[j] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) v[j][i] = 0.f;
+      if (c < S) {
+        l[j] = part_lse[base + c];
+        const float* po = part_o + (base + c) * D + PER_LANE * lane;
+        if constexpr (PER_LANE == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(po);
+          v[j][0] = t.x;
+          v[j][1] = t.y;
+        } else {
+          v[j][0] = po[0];
+        }
       }
     }
+    float mn = m;
+#pragma unroll
+    for (int j = 0; j < U; ++j) mn = fmaxf(mn, l[j]);
+    if (mn == -INFINITY) continue;                  // only empty chunks so far
+    const float sc = __expf(m - mn);                // 0 while m is -inf
+    wsum *= sc;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) acc[i] *= sc;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float w = __expf(l[j] - mn);            // 0 for empty chunks (o = 0 there)
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) acc[i] = fmaf(w, v[j][i], acc[i]);
+    }
+    m = mn;
   }
-  __syncthreads();                                  // red[] reads done
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) acc_sh[wave][PER_LANE * lane + i] = acc[i];
-  if (lane == 0) red[wave] = wsum;
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_w[wave] = wsum;
+  }
   __syncthreads();
   if (wave == 0) {
     const int hk = h / group;                                 // kv head of query head h
-    float tot = 0.f;
+    float M = red_m[0];
 #pragma unroll
-    for (int i = 0; i < kCombineWaves; ++i) tot += red[i];
+    for (int i = 1; i < kCombineWaves; ++i) M = fmaxf(M, red_m[i]);
+    float f[kCombineWaves], tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) {
+      f[i] = (red_m[i] == -INFINITY) ? 0.f : __expf(red_m[i] - M);
+      tot = fmaf(f[i], red_w[i], tot);
+    }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
       const int d = PER_LANE * lane + i;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kCombineWaves; ++w) v += acc_sh[w][d];
+      for (int w = 0; w < kCombineWaves; ++w) v = fmaf(f[w], acc_sh[w][d], v);
       const float vs = per_channel ? v_scale[hk * D + d] : v_scale[hk];
       out[((size_t)r * num_heads + h) * D + d] = from_f32<TO>(v * inv * vs);
     }
