@@ -24,10 +24,12 @@ Modules
   attention  paged gather, exact attention, chunked (split-KV) attention,
              exact max_query_len.
   brute      pure-Python scalar-loop attention for tiny inputs.
+  rotary     rotary position embedding of the new rows and the fused
+             rotate-then-quantize append.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 library special cases, exhaustive enumeration or brute force.  Nothing here is
 "parity unpinned".
 """
 
-from . import codecs, quant, attention, brute  # noqa: F401
+from . import codecs, quant, attention, brute, rotary  # noqa: F401
