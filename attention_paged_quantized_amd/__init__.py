@@ -28,7 +28,7 @@ PATHS = {0: "none", 1: "single", 2: "split", 3: "f32_single", 4: "f32_split", 5:
 # Every symbol include/paq.h declares.
 EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_decode",
            "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
-           "paged_attn_prefill", "kv_quant_append")
+           "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary")
 
 
 class PaqDesc(ctypes.Structure):
@@ -84,6 +84,11 @@ def lib():
         L.kv_quant_append.restype = ctypes.c_int32
         L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
                                       _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
+        L.kv_quant_append_rotary.restype = ctypes.c_int32
+        L.kv_quant_append_rotary.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP,
+                                             _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32P,
+                                             _I32P, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, _VP]
         _lib_handle = L
     return _lib_handle
 
@@ -204,3 +209,21 @@ def kv_quant_append(desc, kv_in_dtype, key, value, key_cache, value_cache, k_sca
         ctypes.byref(desc), dt, _dev(key), _dev(value), _dev(key_cache), _dev(value_cache),
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         _stream(stream)))
+
+
+def kv_quant_append_rotary(desc, kv_in_dtype, query, key, value, key_cache, value_cache,
+                           k_scale, v_scale, block_table, cum_q, past_lens, cum_q_host,
+                           past_lens_host, cos_cache, sin_cache, rotary_dim, interleaved=False,
+                           stream=None):
+    """kv_quant_append with rotary embedding of the new query (in place; None
+    skips it) and key rows first.  cos_cache/sin_cache: fp32 device tensors
+    (max_position, rotary_dim // 2)."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    dt = DTYPES[kv_in_dtype] if isinstance(kv_in_dtype, str) else int(kv_in_dtype)
+    max_position = int(cos_cache.shape[0]) if cos_cache is not None else 0
+    _check(lib().kv_quant_append_rotary(
+        ctypes.byref(desc), dt, _dev(query), _dev(key), _dev(value), _dev(key_cache),
+        _dev(value_cache), _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q),
+        _dev(past_lens), pa, pb, _dev(cos_cache), _dev(sin_cache), max_position, int(rotary_dim),
+        1 if interleaved else 0, _stream(stream)))

@@ -23,6 +23,11 @@ struct AppendArgs {
   int kv_format, scale_mode, in_dtype;
   int max_query_len;   // exact, from the host cum_q
   int tokens_per_wg;
+  // rotary variant only
+  void* query;         // (token_count, num_heads, head_size) q_dtype, rotated in place; or null
+  const float* cos_cache;   // (max_position, rotary_dim / 2)
+  const float* sin_cache;
+  int num_heads, q_dtype, rotary_dim, interleaved;
 };
 
 struct AttnArgs {
@@ -76,6 +81,7 @@ inline int prefill_grid(int max_query_len, int group, int hkv, int batch) {
 }
 
 int launch_quant_append(const AppendArgs& a, hipStream_t st);
+int launch_rotary_append(const AppendArgs& a, hipStream_t st);
 int launch_decode_f32(const AttnArgs& a, hipStream_t st);     // any q_len (portable)
 int launch_decode_mfma(const AttnArgs& a, hipStream_t st);    // q_len in {0,1}
 int launch_combine(const AttnArgs& a, hipStream_t st);

@@ -418,4 +418,73 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
   return launched(paq::launch_quant_append(a, (hipStream_t)stream), "kv_quant_append");
 }
 
+int32_t kv_quant_append_rotary(const paq_desc* d, int32_t kv_in_dtype, void* query,
+                               const void* key, const void* value, void* key_cache,
+                               void* value_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* cum_q,
+                               const int32_t* past_lens, const int32_t* cum_q_host,
+                               const int32_t* past_lens_host, const float* cos_cache,
+                               const float* sin_cache, int32_t max_position,
+                               int32_t rotary_dim, int32_t interleaved, void* stream) {
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_lens_host, &st);
+  if (rc) return rc;
+  if (kv_in_dtype < PAQ_DT_F32 || kv_in_dtype > PAQ_DT_BF16)
+    return fail(PAQ_ERR_INVALID_ARG, "kv_in_dtype %d unknown", kv_in_dtype);
+  if (rotary_dim <= 0 || rotary_dim % 2 || rotary_dim > d->head_size)
+    return fail(PAQ_ERR_INVALID_ARG, "rotary_dim %d must be even and in [2, head_size %d]",
+                rotary_dim, d->head_size);
+  if (rotary_dim % 16)
+    return fail(PAQ_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", rotary_dim);
+  if (interleaved != 0 && interleaved != 1)
+    return fail(PAQ_ERR_INVALID_ARG, "interleaved %d must be 0 or 1", interleaved);
+  if (max_position < 1) return fail(PAQ_ERR_INVALID_ARG, "max_position %d < 1", max_position);
+  for (int b = 0; b < d->batch; ++b) {
+    const int64_t last = (int64_t)past_lens_host[b] + cum_q_host[b + 1] - cum_q_host[b] - 1;
+    if (cum_q_host[b + 1] > cum_q_host[b] && last >= max_position)
+      return fail(PAQ_ERR_INVALID_ARG, "sequence %d reaches position %lld >= max_position %d", b,
+                  (long long)last, max_position);
+  }
+  if (st.max_q == 0) return PAQ_OK;
+  if (!key || !value || !key_cache || !value_cache || !k_scale || !v_scale || !block_table ||
+      !cum_q || !past_lens || !cos_cache || !sin_cache)
+    return fail(PAQ_ERR_INVALID_ARG, "a device pointer argument is NULL");
+  if (((uintptr_t)cos_cache | (uintptr_t)sin_cache) & 15)
+    return fail(PAQ_ERR_INVALID_ARG, "cos_cache and sin_cache must be 16-byte aligned");
+  paq::AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.cum_q = cum_q;
+  a.past_lens = past_lens;
+  a.batch = d->batch;
+  a.hkv = d->kv_num_heads;
+  a.head_size = d->head_size;
+  a.block_size = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.kv_format = d->kv_format;
+  a.scale_mode = d->scale_mode;
+  a.in_dtype = kv_in_dtype;
+  a.max_query_len = st.max_q;
+  a.query = query;
+  a.cos_cache = cos_cache;
+  a.sin_cache = sin_cache;
+  a.num_heads = d->num_heads;
+  a.q_dtype = d->q_dtype;
+  a.rotary_dim = rotary_dim;
+  a.interleaved = interleaved;
+  // work units of one token: query pairs, key units, value chunks
+  const int ur = interleaved ? rotary_dim / 8 : rotary_dim / 16;
+  const int per_tok = (query ? d->num_heads * ur : 0) +
+                      d->kv_num_heads * (ur + (d->head_size - rotary_dim) / 8) +
+                      d->kv_num_heads * d->head_size / 8;
+  a.tokens_per_wg = std::max(1, 2048 / per_tok);
+  return launched(paq::launch_rotary_append(a, (hipStream_t)stream), "kv_quant_append_rotary");
+}
+
 }  // extern "C"

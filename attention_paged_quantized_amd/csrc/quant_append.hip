@@ -13,27 +13,12 @@
 //
 // Memory-bound: each thread converts 8 consecutive channels of one (token,
 // kv head) row of K or V: one 16- or 32-byte load, one 8- or 4-byte store.
-#include "device.hpp"
+#include "append.hpp"
 #include "launch.hpp"
 
 namespace paq {
 
 constexpr int kAppendThreads = 256;
-
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
-  if constexpr (sizeof(T) == 2) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = to_f32(e[i]);
-  } else {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-  }
-}
 
 template <int KVF, int SM, typename TI>
 __global__ __launch_bounds__(kAppendThreads) void quant_append_kernel(
@@ -61,47 +46,12 @@ __global__ __launch_bounds__(kAppendThreads) void quant_append_kernel(
     const int h = rem / (head_size / 8);
     const int d0 = (rem % (head_size / 8)) * 8;
     const TI* src = (is_v ? value : key) + ((size_t)(q0 + tok) * hkv + h) * head_size + d0;
-    const float* sc = is_v ? vscale : kscale;
-    float x[8];
+    float x[8], s[8];
     load8(src, x);
-    float s[8];
-    if constexpr (SM == SCALE_CHANNEL) {
-      f32x4 a = *reinterpret_cast<const f32x4*>(sc + h * head_size + d0);
-      f32x4 c = *reinterpret_cast<const f32x4*>(sc + h * head_size + d0 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { s[i] = a[i]; s[4 + i] = c[i]; }
-    } else {
-      const float v = sc[h];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = v;
-    }
-    const int t = past + tok;
-    const int blk = block_table[(size_t)b * max_blocks + t / block_size];
-    uint8_t* dst = (is_v ? vcache : kcache) +
-                   (((size_t)blk * block_size + t % block_size) * hkv + h) * C;
-    if constexpr (KVF == KV_INT8) {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0 |= (uint32_t)(quant_int(x[i] / s[i], 127.0f) & 0xFF) << (8 * i);
-        w1 |= (uint32_t)(quant_int(x[4 + i] / s[4 + i], 127.0f) & 0xFF) << (8 * i);
-      }
-      *reinterpret_cast<u32x2*>(dst + d0) = (u32x2){w0, w1};
-    } else if constexpr (KVF == KV_INT4) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w |= (uint32_t)(quant_int(x[i] / s[i], 7.0f) & 0xF) << (4 * i);
-      *reinterpret_cast<uint32_t*>(dst + d0 / 2) = w;
-    } else {
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0 |= e4m3_encode(x[i] / s[i]) << (8 * i);
-        w1 |= e4m3_encode(x[4 + i] / s[4 + i]) << (8 * i);
-      }
-      *reinterpret_cast<u32x2*>(dst + d0) = (u32x2){w0, w1};
-    }
+    load_scales8<SM>(is_v ? vscale : kscale, h, head_size, d0, s);
+    uint8_t* row = cache_row(is_v ? vcache : kcache, block_table, b, max_blocks, past + tok,
+                             block_size, hkv, h, C);
+    store_codes8<KVF>(row, d0, x, s);
   }
 }
 

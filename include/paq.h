@@ -3,7 +3,8 @@
  *
  * Three operations over a block-paged KV cache stored as INT8, packed INT4 or
  * FP8 E4M3 with fp32 scales:
- *   kv_quant_append     quantize a step's new key/value rows into their slots;
+ *   kv_quant_append     quantize a step's new key/value rows into their slots
+ *                       (kv_quant_append_rotary: rotary embedding first);
  *   paged_attn_decode   GQA decode (one new token per sequence), single pass or
  *                       split-KV ("flash decoding") with a log-sum-exp merge;
  *   paged_attn_prefill  ragged, causal, chunked prefill.
@@ -195,6 +196,40 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
                         const int32_t* block_table, const int32_t* cum_q,
                         const int32_t* past_lens, const int32_t* cum_q_host,
                         const int32_t* past_lens_host, void* stream);
+
+/* kv_quant_append with rotary position embedding (RoPE) of the new rows first,
+ * in the same launch.  The step just before attention; "PagedAttention FA
+ * path: exact max_query_len" (sections 1-2) shows the rotary kernel dropping
+ * rows when its grid came from the heuristic token_count - batch + 1 and a
+ * sequence had no new token: this grid, like every grid here, comes from the
+ * exact max_query_len of cum_q_host.
+ *   query        (token_count, num_heads, head_size), dtype d->q_dtype, device;
+ *                rotated in place (each element rounded half-even to q_dtype).
+ *                NULL rotates the keys only.
+ *   key, value   as for kv_quant_append; keys are rotated before they are
+ *                quantized, values are appended unchanged.
+ *   cos_cache,
+ *   sin_cache    fp32 (max_position, rotary_dim / 2), device, 16-byte aligned:
+ *                the angle of pair k at position p is [p * rotary_dim/2 + k].
+ *   rotary_dim   channels 0..rotary_dim-1 rotate, the rest pass through; even,
+ *                <= head_size (PAQ_ERR_INVALID_ARG otherwise) and a multiple of
+ *                16 (PAQ_ERR_UNSUPPORTED otherwise).
+ *   interleaved  0: pair k is channels (k, k + rotary_dim/2); 1: (2k, 2k+1).
+ * Row i of sequence b has position past_b + i (the position its key is stored
+ * at), which must be < max_position (checked on the host: PAQ_ERR_INVALID_ARG).
+ * A pair (x, y) becomes x' = fl32(fl32(x*c) - fl32(y*s)), y' = fl32(fl32(y*c) +
+ * fl32(x*s)), c and s its table entries: every product and sum rounded to fp32,
+ * no fused multiply-add, so the key codes (quantized from x' as in
+ * kv_quant_append) are reproducible bit for bit.  Same ownership, stream and
+ * error rules as the other calls; query, key and value must not overlap. */
+int32_t kv_quant_append_rotary(const paq_desc* d, int32_t kv_in_dtype, void* query,
+                               const void* key, const void* value, void* key_cache,
+                               void* value_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* cum_q,
+                               const int32_t* past_lens, const int32_t* cum_q_host,
+                               const int32_t* past_lens_host, const float* cos_cache,
+                               const float* sin_cache, int32_t max_position,
+                               int32_t rotary_dim, int32_t interleaved, void* stream);
 
 #ifdef __cplusplus
 }

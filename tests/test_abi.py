@@ -123,6 +123,14 @@ def _call_append(d, cum, past, in_dtype=1, ptr=FAKE):
                              ptr, pa, pb, None)
 
 
+def _call_rotary(d, cum, past, rd=64, il=0, maxpos=4096, ptr=FAKE, cs=FAKE, query=FAKE):
+    L = paq.lib()
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    return L.kv_quant_append_rotary(ctypes.byref(d), 1, query, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                    ptr, ptr, pa, pb, cs, cs, maxpos, rd, il, None)
+
+
 BAD_CASES = [
     # (description, desc kwargs, q_lens/cum, past, expected status)
     ("cum_q decreases", dict(B=3, T=2), [0, 2, 1, 2], [1, 1, 1], paq.PAQ_ERR_INVALID_ARG),
@@ -146,6 +154,30 @@ def test_invalid_arguments_are_rejected_before_launch(name, kw, cum, past, statu
     assert paq.paq_last_error()
     assert _call_prefill(d, cum, past) == status
     assert _call_append(d, cum, past) == status
+    assert _call_rotary(d, cum, past) == status
+
+
+def test_rotary_specific_checks():
+    d = _desc(2, 2)
+    cum, past = [0, 1, 2], [4, 9]
+    for rd in (0, -16, 3, 130, 144):                     # odd, non-positive, > head_size
+        assert _call_rotary(d, cum, past, rd=rd) == paq.PAQ_ERR_INVALID_ARG, rd
+    assert _call_rotary(d, cum, past, rd=24) == paq.PAQ_ERR_UNSUPPORTED
+    assert "multiple of 16" in paq.paq_last_error()
+    assert _call_rotary(d, cum, past, il=2) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_rotary(d, cum, past, maxpos=0) == paq.PAQ_ERR_INVALID_ARG
+    # the last new row of sequence 1 sits at position 9: a table of 9 rows is short
+    assert _call_rotary(d, cum, past, maxpos=9) == paq.PAQ_ERR_INVALID_ARG
+    assert "position 9" in paq.paq_last_error()
+    # an empty sequence needs no table row, whatever its past
+    assert _call_rotary(_desc(2, 1), [0, 1, 1], [4, 1000], maxpos=5, cs=FAKE + 4) == \
+        paq.PAQ_ERR_INVALID_ARG                          # misaligned tables
+    assert "aligned" in paq.paq_last_error()
+    assert _call_rotary(d, cum, past, cs=None) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_rotary(d, cum, past, ptr=None) == paq.PAQ_ERR_INVALID_ARG
+    # nothing to do: no launch, NULL pointers accepted
+    assert _call_rotary(_desc(2, 0), [0, 0, 0], [4, 9], ptr=None, cs=None, query=None) == \
+        paq.PAQ_OK
 
 
 def test_decode_specific_checks():

@@ -252,3 +252,12 @@ def custom(name, seed, *, batch, num_heads, kv_num_heads, head_size, block_size,
                    num_splits=num_splits, kind=kind, spare=spare,
                    gains=kv_format != "fp8", key_scale_override=key_scale,
                    key_code_sigma=key_code_sigma)
+
+
+def rope_tables(max_position, rotary_dim, base=10000.0):
+    """fp32 cos/sin tables (max_position, rotary_dim // 2) of the usual rotary
+    angles p * base^(-2k / rotary_dim), computed in fp64 and rounded: inputs
+    of the rotary append, like the other seeded inputs here."""
+    k = np.arange(rotary_dim // 2, dtype=np.float64)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * base ** (-2.0 * k / rotary_dim)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
