@@ -11,8 +11,9 @@
 // round-half-even saturating to +-448.  `x / s` is IEEE fp32 division (the
 // library is built without fast-math, so it is correctly rounded).
 //
-// Memory-bound: each thread converts 8 consecutive channels of one (token,
-// kv head) row of K or V: one 16- or 32-byte load, one 8- or 4-byte store.
+// Memory-bound: a thread converts 8 consecutive channels of one kv head of K
+// or V (one 16- or 32-byte load, one 8- or 4-byte store per token) for the
+// tokens of its workgroup, eight tokens' loads in flight at a time.
 #include "append.hpp"
 #include "launch.hpp"
 
@@ -37,21 +38,39 @@ __global__ __launch_bounds__(kAppendThreads) void quant_append_kernel(
   const int chunks_per_row = hkv * head_size / 8;           // per tensor
   const int chunk_per_tok = 2 * chunks_per_row;              // K and V
   const int C = (KVF == KV_INT4) ? head_size / 2 : head_size;
-  const int total = (i_end - i_begin) * chunk_per_tok;
-  for (int idx = threadIdx.x; idx < total; idx += kAppendThreads) {
-    const int tok = i_begin + idx / chunk_per_tok;
-    int rem = idx % chunk_per_tok;
-    const bool is_v = rem >= chunks_per_row;
-    if (is_v) rem -= chunks_per_row;
-    const int h = rem / (head_size / 8);
-    const int d0 = (rem % (head_size / 8)) * 8;
-    const TI* src = (is_v ? value : key) + ((size_t)(q0 + tok) * hkv + h) * head_size + d0;
-    float x[8], s[8];
-    load8(src, x);
+  // A thread keeps one chunk (8 channels of one kv head of K or V) and walks
+  // the workgroup's tokens, kUnroll at a time with all their loads issued
+  // before the first store; neighbouring lanes take neighbouring chunks.
+  constexpr int kUnroll = 8;
+  for (int c = threadIdx.x; c < chunk_per_tok; c += kAppendThreads) {
+    const bool is_v = c >= chunks_per_row;
+    const int cc = is_v ? c - chunks_per_row : c;
+    const int h = cc / (head_size / 8), d0 = (cc % (head_size / 8)) * 8;
+    const TI* src = (is_v ? value : key) + ((size_t)q0 * hkv + h) * head_size + d0;
+    uint8_t* cache = (is_v ? vcache : kcache) + (size_t)h * C;
+    const int32_t* table = block_table + (size_t)b * max_blocks;
+    float s[8];
     load_scales8<SM>(is_v ? vscale : kscale, h, head_size, d0, s);
-    uint8_t* row = cache_row(is_v ? vcache : kcache, block_table, b, max_blocks, past + tok,
-                             block_size, hkv, h, C);
-    store_codes8<KVF>(row, d0, x, s);
+    auto dst = [&](int t, int blk) {
+      return cache + ((size_t)blk * block_size + t % block_size) * hkv * C;
+    };
+    int i = i_begin;
+    for (; i + kUnroll <= i_end; i += kUnroll) {
+      float x[kUnroll][8];
+      int blk[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        load8(src + (size_t)(i + j) * hkv * head_size, x[j]);
+        blk[j] = table[(past + i + j) / block_size];
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) store_codes8<KVF>(dst(past + i + j, blk[j]), d0, x[j], s);
+    }
+    for (; i < i_end; ++i) {
+      float x[8];
+      load8(src + (size_t)i * hkv * head_size, x);
+      store_codes8<KVF>(dst(past + i, table[(past + i) / block_size]), d0, x, s);
+    }
   }
 }
 

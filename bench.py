@@ -33,7 +33,10 @@ MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, 256 CU x 4096 flop
 KERNEL_SOURCES = {
     "decode": ["decode_mfma.hip", "combine.hip", "device.hpp", "launch.hpp"],
     "prefill": ["prefill_mfma.hip", "device.hpp", "launch.hpp"],
+    "quant_append_kernel": ["quant_append.hip", "append.hpp", "device.hpp", "launch.hpp"],
+    "rotary_append_kernel": ["rotary_append.hip", "append.hpp", "device.hpp", "launch.hpp"],
 }
+MAIN_KERNEL = {"decode": "decode_stream_kernel", "prefill": "prefill_mfma_kernel"}
 
 
 def parse():
@@ -59,12 +62,26 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then "
                          "WRITE_SIZE) into profiles/counters_<workload>.json and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--rotary", action="store_true",
+                    help="the step's append is kv_quant_append_rotary (rotary embedding of "
+                         "the new query and key rows over all head_size channels)")
     return ap.parse_args()
 
 
 def kv_bytes(w):
     act = w.q_lens > 0
     return int((w.kv_lens[act].astype(np.int64)).sum()) * w.kv_num_heads * 2 * w.cache_head_size
+
+
+def append_bytes(w, T, rotary):
+    """Algorithmic HBM bytes of one append: the new key and value rows read,
+    their codes written; with the rotary embedding also the query rows read
+    and written back and one cos and one sin table row per new row."""
+    ib = {"f32": 4, "f16": 2, "bf16": 2}
+    n = 2 * T * w.kv_num_heads * (w.head_size * ib[w.kv_in_dtype] + w.cache_head_size)
+    if rotary:
+        n += 2 * T * w.num_heads * w.head_size * ib[w.q_dtype] + T * w.head_size * 4
+    return int(n)
 
 
 def prefill_flops(w):
@@ -82,14 +99,15 @@ def source_sha(kind):
     return h.hexdigest()[:16]
 
 
-def counters(workload, kind, launch_bytes):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
-    import glob
-    found = glob.glob(os.path.join(ROOT, "profiles", "*_%s_counters.json" % workload))
-    if len(found) != 1:
+def counters(workload, kind):
+    """HBM traffic per launch from committed rocprofv3 counter runs of the
+    workload's main kernel of this kind (decode, prefill, or an append kernel's
+    name), if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.json" %
+                        (MAIN_KERNEL.get(kind, kind), workload))
+    if not os.path.exists(path):
         return None
-    with open(found[0]) as f:
+    with open(path) as f:
         c = json.load(f)
     if c.get("source_sha") != source_sha(kind):
         return None
@@ -148,7 +166,8 @@ CALIB_KERNEL = "neg_kernel"
 
 def _short(name):
     for k in ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel",
-              "prefill_mfma_kernel", "quant_append_kernel", CALIB_KERNEL):
+              "prefill_mfma_kernel", "quant_append_kernel", "rotary_append_kernel",
+              CALIB_KERNEL):
         if k in name:
             return k
     return name[:48]
@@ -230,6 +249,19 @@ def summarize_pmc(args):
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print("wrote", out, json.dumps(res))
+    # the append kernel of the same runs, on its own
+    for k in ("quant_append_kernel", "rotary_append_kernel"):
+        if k not in fetch:
+            continue
+        r = {"workload": w.name, "source_sha": source_sha(k), "command": args.command,
+             "calibration": res["calibration"], "fetch_factor": res["fetch_factor"],
+             "write_factor": res["write_factor"], "fetch_kib": fetch[k],
+             "write_kib": write.get(k, 0.0)}
+        r["hbm_bytes_per_call"] = int((r["fetch_kib"] * ff + r["write_kib"] * wf) * 1024)
+        out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (k, w.name))
+        with open(out, "w") as f:
+            json.dump(r, f, indent=1)
+        print("wrote", out, json.dumps(r))
 
 
 CALIB_ELEMS = 2 ** 26          # fp32 elements of the counter-calibration copy (256 MiB)
@@ -283,6 +315,9 @@ def main():
           flush=True)
 
     desc = desc_for(w, T)
+    if args.rotary:
+        rcos, rsin = workloads.rope_tables(int(w.kv_lens.max()) + 1, w.head_size)
+        rcos, rsin = torch.from_numpy(rcos).to(dev), torch.from_numpy(rsin).to(dev)
     kin = w.new_key.to(dev)
     vin = w.new_value.to(dev)
     outs = [torch.empty_like(g.query) for g in devs]
@@ -303,21 +338,34 @@ def main():
                                    g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0,
                                    stream)
 
+    def append(g):
+        if args.rotary:
+            paq.kv_quant_append_rotary(desc, w.kv_in_dtype, g.query, kin, vin, g.kc, g.vc,
+                                       g.k_scale, g.v_scale, g.block_table, g.cum_q, g.past,
+                                       w.cum_q, w.past_lens, rcos, rsin, w.head_size, False,
+                                       stream)
+        else:
+            paq.kv_quant_append(desc, w.kv_in_dtype, kin, vin, g.kc, g.vc, g.k_scale,
+                                g.v_scale, g.block_table, g.cum_q, g.past, w.cum_q,
+                                w.past_lens, stream)
+
     def step(i, ev=None):
         g = devs[i % pools]
-        paq.kv_quant_append(desc, w.kv_in_dtype, kin, vin, g.kc, g.vc, g.k_scale, g.v_scale,
-                            g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, stream)
+        append(g)
         if ev is not None:
             ev[0].record(stream)
         attention(g, outs[i % pools])
         if ev is not None:
             ev[1].record(stream)
 
-    # Warm up, and measure how long the host takes to queue one step.
+    # Warm up, and measure how long the host takes to queue one step (with
+    # its events, as in the timed loop).
+    wevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.warmup)]
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     for i in range(args.warmup):
-        step(i)
+        step(i, wevs[i])
     host_ms = (time.perf_counter() - h0) * 1e3 / max(1, args.warmup)
     torch.cuda.synchronize()
     hz = sleep_rate(stream)
@@ -325,7 +373,7 @@ def main():
     def hold(n_steps):
         # keep the stream busy while the host queues n_steps, so that the
         # events below time the GPU and not the Python launch rate
-        torch.cuda._sleep(int((2.0 * n_steps * host_ms + 2.0) * 1e-3 * hz))
+        torch.cuda._sleep(int((3.0 * n_steps * host_ms + 2.0) * 1e-3 * hz))
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -343,6 +391,18 @@ def main():
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
+    # the append on its own: per-call events over the same pools, outside the
+    # timed steps (its events would add to their time)
+    aevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    hold(args.steps)
+    for i, (e0, e1) in enumerate(aevs):
+        e0.record(stream)
+        append(devs[i % pools])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    app_avg = sum(a.elapsed_time(b) for a, b in aevs) / len(aevs)
 
     # warm (cache-resident) reference: the same pool every call, per-call events
     warm_ms = None
@@ -397,7 +457,7 @@ def main():
         cfg.update({"num_splits": S, "kv_bytes_per_step": kvb,
                     "max_kv_len": int(w.kv_lens.max())})
         achieved = kvb / (kern_avg / 1e3) / 1e9
-        traffic = counters(w.name, "decode", kvb)
+        traffic = counters(w.name, "decode")
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -416,13 +476,21 @@ def main():
         achieved = fl / (kern_avg / 1e3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                               "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                              "traffic": counters(w.name, "prefill", fl),
+                              "traffic": counters(w.name, "prefill"),
                               "kernel": "paged_attn_prefill call (prefill_mfma_kernel)",
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
                               "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
                               "algorithmic_flops_per_launch": fl}
         cfg.update({"max_query_len": int(w.q_lens.max()), "causal": True})
     result["config"] = cfg
+    ab = append_bytes(w, T, args.rotary)
+    result["append"] = {"kernel": "rotary_append_kernel" if args.rotary else "quant_append_kernel",
+                        "bound": "hbm", "us_avg": round(app_avg * 1e3, 3),
+                        "algorithmic_bytes": ab,
+                        "achieved": round(ab / (app_avg / 1e3) / 1e9, 2), "unit": "GB/s",
+                        "frac": round(ab / (app_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": counters(w.name, "rotary_append_kernel" if args.rotary
+                                            else "quant_append_kernel")}
     result["hbm_copy_GBs"] = round(copy_gbs, 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (%.0f s budget)" % args.cpu_seconds,
