@@ -180,6 +180,8 @@ def summarize_stats(args):
     w = workloads.make(args.workload)
     rows = list(csv.DictReader(open(args.summarize_stats)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    if args.rotary:
+        return summarize_append_stats(args, w, rows, "rotary_append_kernel")
     call = [r for r in rows if any(k in r["Name"] for k in CALL_KERNELS[w.kind])]
     main_k = _short(call[0]["Name"]) if call else "none"
     lines = ["rocprofv3 kernel statistics, workload %s (%s)" % (w.name, w.kind),
@@ -209,6 +211,32 @@ def summarize_stats(args):
     print("wrote", out)
 
 
+def summarize_append_stats(args, w, rows, kernel):
+    """The append kernel's line of a kernel-statistics run ->
+    profiles/<kernel>_<workload>.txt"""
+    mine = [r for r in rows if kernel in r["Name"]]
+    r = mine[0]
+    avg = float(r["AverageNs"]) / 1e3
+    ab = append_bytes(w, w.token_count, kernel == "rotary_append_kernel")
+    lines = ["rocprofv3 kernel statistics, workload %s, %s" % (w.name, kernel),
+             "command: %s" % (args.command or "(not recorded)"),
+             "kernel sources sha256[:16]: %s" % source_sha(kernel), "",
+             "%-22s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us",
+                                                 "max_us", "total_us")]
+    for q in rows[:12]:
+        lines.append("%-22s %7d %12.3f %12.3f %12.3f %12.1f" % (
+            _short(q["Name"]), int(q["Calls"]), float(q["AverageNs"]) / 1e3,
+            float(q["MinNs"]) / 1e3, float(q["MaxNs"]) / 1e3, float(q["TotalDurationNs"]) / 1e3))
+    lines += ["", "%s: %.3f us average per call (min %.3f)" % (kernel, avg,
+                                                               float(r["MinNs"]) / 1e3),
+              "algorithmic bytes per call %d -> %.1f GB/s, %.4f of %.0f GB/s" %
+              (ab, ab / (avg * 1e3), ab / (avg * 1e3) / HBM_PEAK_GBS, HBM_PEAK_GBS)]
+    out = os.path.join(ROOT, "profiles", "%s_%s.txt" % (kernel, w.name))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out)
+
+
 def summarize_pmc(args):
     """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) -> per-call HBM bytes of
     the attention kernels, scaled by the counters of a 256 MiB copy, written to
@@ -232,6 +260,8 @@ def summarize_pmc(args):
     ff = calib_kib / fetch[CALIB_KERNEL]
     wf = calib_kib / write[CALIB_KERNEL]
     ks = [k for k in CALL_KERNELS[w.kind] if k in fetch]
+    if args.rotary:
+        ks = []                     # a rotary run records its append kernel only
     res = {"workload": w.name, "source_sha": source_sha(w.kind), "command": args.command,
            "calibration": "torch.neg over %d fp32 (%.0f KiB read, %.0f KiB written): "
                           "FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" %
@@ -245,12 +275,13 @@ def summarize_pmc(args):
     if w.kind == "decode":
         res["algorithmic_kv_bytes_per_call"] = kv_bytes(w)
         res["traffic_over_algorithmic"] = round(hbm / kv_bytes(w), 4)
-    out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (ks[0], w.name))
-    with open(out, "w") as f:
-        json.dump(res, f, indent=1)
-    print("wrote", out, json.dumps(res))
+    if ks:
+        out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (ks[0], w.name))
+        with open(out, "w") as f:
+            json.dump(res, f, indent=1)
+        print("wrote", out, json.dumps(res))
     # the append kernel of the same runs, on its own
-    for k in ("quant_append_kernel", "rotary_append_kernel"):
+    for k in ("rotary_append_kernel",) if args.rotary else ("quant_append_kernel",):
         if k not in fetch:
             continue
         r = {"workload": w.name, "source_sha": source_sha(k), "command": args.command,
@@ -258,6 +289,9 @@ def summarize_pmc(args):
              "write_factor": res["write_factor"], "fetch_kib": fetch[k],
              "write_kib": write.get(k, 0.0)}
         r["hbm_bytes_per_call"] = int((r["fetch_kib"] * ff + r["write_kib"] * wf) * 1024)
+        ab = append_bytes(w, w.token_count, k == "rotary_append_kernel")
+        r["algorithmic_bytes_per_call"] = ab
+        r["traffic_over_algorithmic"] = round(r["hbm_bytes_per_call"] / ab, 4)
         out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (k, w.name))
         with open(out, "w") as f:
             json.dump(r, f, indent=1)
