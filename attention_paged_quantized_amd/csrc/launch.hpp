@@ -46,6 +46,8 @@ struct AttnArgs {
   int q_dtype, kv_format, scale_mode;
   int num_splits;       // 1 = single pass (no partials)
   int part_count;       // split-KV: partials per (row, head) in the workspace
+  int grid_x;           // launch grid (1-D prefill: from the host plan)
+  int pf_ntq;           // prefill: query tiles of every sequence if all have the same, else 0
   int max_query_len;    // exact, from the host cum_q
   int max_kv_len;       // longest sequence with new rows (host)
   int block_size_log2;  // block_size is a power of two
@@ -70,14 +72,33 @@ inline int decode_split_waves(int hkv, int heads_per_wave, int batch, int splits
   const long waves = (long)(hkv / heads_per_wave) * batch * splits;
   return waves >= 8L * (num_cus > 0 ? num_cus : 256) ? 8 : 4;
 }
-// Prefill (MFMA): workgroups of 4 waves x 32 / group tokens; a 1-D grid of
-// 8 XCDs x ceil(pairs / 8) (sequence, kv head) pairs x query tiles per pair.
+// Prefill (MFMA): workgroups of 4 waves x 32 / group tokens.  (Sequence, kv
+// head) pair p runs on XCD p % 8 and needs ceil(q_len / tokens) query tiles;
+// the 1-D grid is 8 x the largest per-XCD tile count, so no workgroup is
+// launched for a tile past its sequence's new rows.
 constexpr int kPrefillWaves = 4;
 inline int prefill_tokens_per_workgroup(int group) { return kPrefillWaves * (32 / group); }
-inline int prefill_grid(int max_query_len, int group, int hkv, int batch) {
+inline int prefill_grid(const int32_t* cum_q_host, int batch, int group, int hkv) {
   const int tok = prefill_tokens_per_workgroup(group);
-  const long pairs = (long)hkv * batch;
-  return (int)(8 * ((pairs + 7) / 8) * ((max_query_len + tok - 1) / tok));
+  long items[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (long pr = 0; pr < (long)hkv * batch; ++pr) {
+    const int b = (int)(pr / hkv);
+    items[pr % 8] += (cum_q_host[b + 1] - cum_q_host[b] + tok - 1) / tok;
+  }
+  long m = 0;
+  for (int x = 0; x < 8; ++x) m = items[x] > m ? items[x] : m;
+  return (int)(8 * m);
+}
+// The common query-tile count of all sequences, or 0 when they differ.
+inline int prefill_uniform_tiles(const int32_t* cum_q_host, int batch, int group) {
+  const int tok = prefill_tokens_per_workgroup(group);
+  int n = -1;
+  for (int b = 0; b < batch; ++b) {
+    const int t = (cum_q_host[b + 1] - cum_q_host[b] + tok - 1) / tok;
+    if (n >= 0 && t != n) return 0;
+    n = t;
+  }
+  return n > 0 ? n : 0;
 }
 
 int launch_quant_append(const AppendArgs& a, hipStream_t st);

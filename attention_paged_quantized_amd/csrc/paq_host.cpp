@@ -215,7 +215,7 @@ int plan_prefill(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pa
   if (d->q_dtype != PAQ_DT_F32 &&
       paq::prefill_mfma_supports(d->head_size, group, d->block_size, d->q_dtype)) {
     p->path = PAQ_PATH_PREFILL;
-    p->grid_x = paq::prefill_grid(st.max_q, group, d->kv_num_heads, d->batch);
+    p->grid_x = paq::prefill_grid(cum_q_host, d->batch, group, d->kv_num_heads);
     p->grid_y = 1;
     p->grid_z = 1;
   } else {
@@ -255,6 +255,7 @@ paq::AttnArgs attn_args(const paq_desc* d, const void* query, void* out, const v
   a.num_splits = p.num_splits > 0 ? p.num_splits : 1;
   a.max_query_len = p.max_query_len;
   a.max_kv_len = p.max_kv_len;
+  a.grid_x = p.grid_x;
   a.block_size_log2 = __builtin_ctz((unsigned)d->block_size);
   a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d->head_size);
   return a;
@@ -374,7 +375,10 @@ int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
   paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
                               block_table, cum_q, past_lens, softmax_scale, p);
   hipStream_t st = (hipStream_t)stream;
-  if (p.path == PAQ_PATH_PREFILL) return launched(paq::launch_prefill_mfma(a, st), "prefill (MFMA)");
+  if (p.path == PAQ_PATH_PREFILL) {
+    a.pf_ntq = paq::prefill_uniform_tiles(cum_q_host, d->batch, d->num_heads / d->kv_num_heads);
+    return launched(paq::launch_prefill_mfma(a, st), "prefill (MFMA)");
+  }
   return launched(paq::launch_decode_f32(a, st), "prefill (fp32)");
 }
 

@@ -196,6 +196,40 @@ __device__ __forceinline__ int32_t choose(bool c, int32_t a, int32_t b) {
   return b ^ ((a ^ b) & -(int32_t)c);
 }
 
+// The (pair, query tile) item of prefill workgroup i as pair << 32 | tile, or
+// -1 past its XCD's items (see the kernel for the order).  Not inlined: the
+// search runs once per workgroup, and kept apart it leaves the register
+// allocation of the kernel's main loop as it is.
+__device__ __attribute__((noinline)) long long prefill_find_item(const int32_t* __restrict__ cum_q,
+                                                           int P, int hkv, int TOK, int i) {
+  const int x = i % 8, k = i / 8;
+  const int lane = (int)(threadIdx.x & 63);
+  int before = 0;
+  for (int j0 = 0; x + 8 * j0 < P; j0 += 64) {
+    const int pr = x + 8 * (j0 + lane);
+    int cnt = 0;
+    if (pr < P) {
+      const int sb = pr / hkv;
+      cnt = (cum_q[sb + 1] - cum_q[sb] + TOK - 1) / TOK;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const unsigned long long hit = __ballot(before + incl > k);
+    if (hit) {
+      const int l = (int)__builtin_ctzll(hit);
+      const int incl_l = __shfl(incl, l, 64), cnt_l = __shfl(cnt, l, 64);
+      return ((long long)(x + 8 * (j0 + l)) << 32) |
+             (long long)(cnt_l - 1 - (k - (before + incl_l - cnt_l)));
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  return -1;
+}
+
 template <int D, int KVF, int SM, typename TQ, typename TK, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
@@ -214,17 +248,31 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // head) pairs x, x + 8, x + 16, ... (with 8 kv heads: one head of every
   // sequence, which balances ragged batches across XCDs); all query tiles of a
   // pair run on its XCD and re-read the pair's keys and values from that L2,
-  // the pair's heaviest tiles first.
-  const int ntq = (a.max_query_len + TOK - 1) / TOK;          // query tiles per pair
-  const int k = (int)(blockIdx.x / 8);
-  const int pair = (int)(blockIdx.x % 8) + 8 * (k / ntq);
-  if (pair >= a.hkv * a.batch) return;
-  const int qt = ntq - 1 - k % ntq;
+  // the pair's heaviest tiles first.  Workgroup i is item i / 8 of XCD i % 8's
+  // list of (pair, tile) items, pairs in order, each with ceil(q_len / TOK)
+  // tiles: found by a wave-wide prefix sum over the tile counts of the XCD's
+  // pairs, 64 pairs at a time.
+  // When every sequence has the same tile count (pf_ntq > 0) the item is
+  // plain arithmetic.
+  int pair, qt;
+  if (a.pf_ntq > 0) {
+    const int k = (int)(blockIdx.x / 8);
+    pair = (int)(blockIdx.x % 8) + 8 * (k / a.pf_ntq);
+    qt = a.pf_ntq - 1 - k % a.pf_ntq;
+    if (pair >= a.hkv * a.batch) pair = -1;
+  } else {
+    const long long item =
+        prefill_find_item(a.cum_q, a.hkv * a.batch, a.hkv, TOK, (int)blockIdx.x);
+    pair = item < 0 ? -1 : (int)(item >> 32);
+    qt = (int)(item & 0xFFFFFFFFll);
+  }
+  pair = __builtin_amdgcn_readfirstlane(pair);        // uniform: keep it (and all
+  qt = __builtin_amdgcn_readfirstlane(qt);            // derived from it) scalar
+  if (pair < 0) return;                               // past this XCD's items
   const int h = pair % a.hkv, b = pair / a.hkv;
   const int q0 = a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - q0;
   const int tok0 = qt * TOK;
-  if (tok0 >= qlen) return;
   const int past = a.past_lens[b];
   const int H = a.num_heads, hkv = a.hkv, bs = a.block_size, lbs = a.block_size_log2;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -655,10 +703,8 @@ bool prefill_mfma_supports(int head_size, int group, int block_size, int q_dtype
 template <int D, int KVF, int SM, typename TQ, typename TK>
 static int launch_pf(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = kPfWavesPerGroup;
-  const int G = a.num_heads / a.hkv;
-  const int TOK = NW * (32 / G);
   static_assert(NW == kPrefillWaves, "prefill geometry");
-  dim3 grid(prefill_grid(a.max_query_len, G, a.hkv, a.batch), 1, 1);
+  dim3 grid(a.grid_x, 1, 1);                  // from the host plan (exact tile counts)
   hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW>), grid, dim3(NW * 64), 0, st,
                      a, a.block_table);
   return 0;

@@ -85,9 +85,19 @@ def test_plan_prefill_uses_exact_max_query_len():
     d = _desc(3, 5, mb=4)
     p = paq.paq_plan_prefill(d, _cum([5, 0, 0]), [0, 7, 3])
     assert p.max_query_len == 5 and p.active_seqs == 1
-    # one 32-token query tile (4 waves x 8 tokens at group 4) per (sequence, kv
-    # head): 1 x 8 x 3 = 24 workgroups, rounded up to the 8 XCDs
-    assert (p.grid_x, p.grid_y, p.grid_z) == (24, 1, 1)
+    # one 32-token query tile (4 waves x 8 tokens at group 4) for each kv head of
+    # the one sequence with rows: one workgroup on each of the 8 XCDs, none for
+    # the empty sequences
+    assert (p.grid_x, p.grid_y, p.grid_z) == (8, 1, 1)
+    # ragged: q_lens {70, 1, 33} -> 3 + 1 + 2 tiles for every kv head; with 8 kv
+    # heads XCD x takes head x of every sequence: 6 items each
+    p = paq.paq_plan_prefill(_desc(3, 104, mb=8), _cum([70, 1, 33]), [0, 5, 9])
+    assert p.grid_x == 8 * 6
+    # 2 kv heads x 5 sequences = 10 pairs: XCDs 0 and 1 take pairs {0, 8} and
+    # {1, 9} (sequences 0 and 4), the others one pair each
+    p = paq.paq_plan_prefill(_desc(5, 140, H=8, hkv=2, mb=8), _cum([64, 0, 0, 0, 76]),
+                             [0] * 5)
+    assert p.grid_x == 8 * (2 + 3)
     # the exact maximum sizes the grid: 2048 tokens -> 64 query tiles per pair
     p = paq.paq_plan_prefill(_desc(4, 8192, mb=128), _cum([2048] * 4), [0] * 4)
     assert p.grid_x == 64 * 8 * 4
