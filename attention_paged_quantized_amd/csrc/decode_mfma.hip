@@ -229,10 +229,14 @@ template <int KVF, int D, int HW> struct WaveCopy {
   // one physical block (block_size is a multiple of 16, and of 32 when a block
   // holds both halves).
   struct Blocks { int32_t b0, b1; };
+  // table entry of 16-key half `half` of the tile at k0 (clamped into
+  // [0, kend - 1]: an empty range reads entry 0, never used)
+  __device__ __forceinline__ static int entry(int k0, int kend, int lbs, int half) {
+    return max(0, min(k0 + 16 * half, kend - 1)) >> lbs;
+  }
   __device__ __forceinline__ static Blocks blocks(int k0, int kend, int lbs,
                                                  const int32_t* __restrict__ table) {
-    // (clamped into [0, kend - 1]: an empty range reads entry 0, never used)
-    return Blocks{table[max(0, min(k0, kend - 1)) >> lbs], table[max(0, min(k0 + 16, kend - 1)) >> lbs]};
+    return Blocks{table[entry(k0, kend, lbs, 0)], table[entry(k0, kend, lbs, 1)]};
   }
   __device__ __forceinline__ void issue(uint8_t* slot, int k0, int kend, int lbs,
                                         const int32_t* __restrict__ table, const uint8_t* kbase,
@@ -521,39 +525,56 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
   constexpr int NQK = Geo::NQK, NPV = Geo::NPV;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
+  const int lbs = a.block_size_log2;
+  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+  // This wave's key range [kb, ke) and tile stride for a sequence of kv_len
+  // keys.
+  auto wave_range = [&](int kv_len, int& kb, int& ke) {
+    if constexpr (SPLIT) {
+      const int chunk = blockIdx.z * NW + wave;
+      const int nb = (kv_len + a.block_size - 1) >> lbs;
+      if (chunk < a.num_splits) {
+        chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
+      } else {
+        kb = ke = 0;                                      // past the last chunk: empty
+      }
+    } else {
+      kb = 32 * wave;
+      ke = kv_len;
+    }
+  };
+  // The first tile's block ids are read before this sequence's length
+  // arrives, for the batch's longest length (inside the table row either
+  // way); they serve whenever the true range names the same table entries,
+  // which saves the table round trip before the first copy.
+  using WC = WaveCopy<KVF, D, HW>;
+  int kb_s, ke_s;
+  wave_range(a.max_kv_len, kb_s, ke_s);
+  const typename WC::Blocks spec = WC::blocks(kb_s, ke_s, lbs, table);
   const int q0 = a.cum_q[b];
-  if (a.cum_q[b + 1] == q0) return;                       // no new token: no rows
-  const int kv_len = a.past_lens[b] + 1;
+  const int past = a.past_lens[b];
+  // no new token: no rows.  The test also reads the past and the speculative
+  // entries (a negative past never occurs), so all these loads go out
+  // together instead of one behind the other.
+  if ((a.cum_q[b + 1] == q0) | ((past < 0) & (spec.b0 == spec.b1))) return;
+  const int kv_len = past + 1;
   const int hkv = a.hkv, H = a.num_heads;
   const int G = H / hkv;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int lbs = a.block_size_log2;
-  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
   const uint32_t row_stride = (uint32_t)(hkv * Geo::C);   // bytes between tokens
   const uint8_t* kbase = a.key_cache + (size_t)blockIdx.x * SG::RB;
   const uint8_t* vbase = a.value_cache + (size_t)blockIdx.x * SG::RB;
 
-  // this wave's key range [kb, ke) and its tile stride
-  int kb, ke, stride, chunk = 0;
-  if constexpr (SPLIT) {
-    chunk = blockIdx.z * NW + wave;
-    const int nb = (kv_len + a.block_size - 1) >> lbs;
-    if (chunk < a.num_splits) {
-      chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
-    } else {
-      kb = ke = 0;                                        // past the last chunk: empty
-    }
-    stride = 32;
-  } else {
-    kb = 32 * wave;
-    ke = kv_len;
-    stride = 32 * NW;
-  }
+  int kb, ke;
+  wave_range(kv_len, kb, ke);
+  const int stride = SPLIT ? 32 : 32 * NW;
+  const bool spec_ok = WC::entry(kb, ke, lbs, 0) == WC::entry(kb_s, ke_s, lbs, 0) &&
+                       WC::entry(kb, ke, lbs, 1) == WC::entry(kb_s, ke_s, lbs, 1);
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NS * SG::SLOT];
   uint8_t* myring = ring[wave];
-  WaveCopy<KVF, D, HW> cp;
+  WC cp;
   cp.init(lane, row_stride);
 
   // query and key-scale loads go out first, then this wave's first NS tiles
@@ -561,8 +582,11 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
 #pragma unroll
   for (int hh = 0; hh < HW; ++hh)
     load_query<D, SM, TQ>(a, blockIdx.x * HW + hh, q0, G, col, grp, qraw[hh]);
+  if (kb < ke)
+    cp.issue(myring, kb, ke, lbs, spec_ok ? spec : WC::blocks(kb, ke, lbs, table), kbase, vbase,
+             row_stride);
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
+  for (int j = 1; j < NS; ++j)
     if (kb + j * stride < ke)
       cp.issue(myring + j * SG::SLOT, kb + j * stride, ke, lbs, table, kbase, vbase, row_stride);
   // The waits below count NS - 1 tiles in flight behind the current one; with
