@@ -302,14 +302,20 @@ CALIB_ELEMS = 2 ** 26          # fp32 elements of the counter-calibration copy (
 
 
 def sleep_rate(stream):
-    """Cycles per second of torch.cuda._sleep on this device."""
+    """Cycles per second of torch.cuda._sleep on this device: the fastest of a
+    few calibrations (its cycles follow the shader clock, which may still be
+    ramping up at the first ones; the fastest rate gives the shortest sleep
+    per cycle, so holds sized from it are never too short)."""
     import torch
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    torch.cuda._sleep(2_000_000)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return 2_000_000 / (e0.elapsed_time(e1) / 1e3)
+    rates = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(2_000_000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(2_000_000 / (e0.elapsed_time(e1) / 1e3))
+    return max(rates)
 
 
 def main():
@@ -407,7 +413,8 @@ def main():
     def hold(n_steps):
         # keep the stream busy while the host queues n_steps, so that the
         # events below time the GPU and not the Python launch rate
-        torch.cuda._sleep(int((3.0 * n_steps * host_ms + 2.0) * 1e-3 * hz))
+        # (a generous margin: the sleep is outside the timed region)
+        torch.cuda._sleep(int((6.0 * n_steps * host_ms + 20.0) * 1e-3 * hz))
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
