@@ -28,7 +28,8 @@ PATHS = {0: "none", 1: "single", 2: "split", 3: "f32_single", 4: "f32_split", 5:
 # Every symbol include/paq.h declares.
 EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_decode",
            "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
-           "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary")
+           "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary",
+           "paged_attn_decode_host")
 
 
 class PaqDesc(ctypes.Structure):
@@ -84,6 +85,10 @@ def lib():
         L.kv_quant_append.restype = ctypes.c_int32
         L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
                                       _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
+        L.paged_attn_decode_host.restype = ctypes.c_int32
+        L.paged_attn_decode_host.argtypes = [ctypes.POINTER(PaqDesc), _VP, _VP, _VP, _VP, _VP,
+                                             _VP, _VP, _VP, _VP, ctypes.c_float,
+                                             ctypes.c_int32, ctypes.c_int32]
         L.kv_quant_append_rotary.restype = ctypes.c_int32
         L.kv_quant_append_rotary.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP,
                                              _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32P,
@@ -227,3 +232,25 @@ def kv_quant_append_rotary(desc, kv_in_dtype, query, key, value, key_cache, valu
         _dev(value_cache), _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q),
         _dev(past_lens), pa, pb, _dev(cos_cache), _dev(sin_cache), max_position, int(rotary_dim),
         1 if interleaved else 0, _stream(stream)))
+
+
+def paged_attn_decode_host(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                           block_table, cum_q, past_lens, softmax_scale=0.0, num_splits=0,
+                           num_threads=0):
+    """Decode on the host CPU.  Every array is a host numpy array: query/out
+    float32 (T, H, D), caches uint8, scales float32, table/cum_q/past int32
+    (C-contiguous; out is written)."""
+    import numpy as np
+
+    def host(x, dtype):
+        if not isinstance(x, np.ndarray) or x.dtype != dtype or not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("expected a C-contiguous %s numpy array" % np.dtype(dtype).name)
+        return x.ctypes.data
+
+    if not out.flags["WRITEABLE"]:
+        raise ValueError("out must be writeable")
+    _check(lib().paged_attn_decode_host(
+        ctypes.byref(desc), host(query, np.float32), host(out, np.float32),
+        host(key_cache, np.uint8), host(value_cache, np.uint8), host(k_scale, np.float32),
+        host(v_scale, np.float32), host(block_table, np.int32), host(cum_q, np.int32),
+        host(past_lens, np.int32), float(softmax_scale), int(num_splits), int(num_threads)))

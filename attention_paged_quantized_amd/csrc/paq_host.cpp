@@ -15,9 +15,11 @@
 
 #include <algorithm>
 #include <mutex>
+#include <thread>
 #include <string>
 
 #include "../../include/paq.h"
+#include "decode_host.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -420,6 +422,53 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
   const int chunks_per_tok = 2 * d->kv_num_heads * d->head_size / 8;
   a.tokens_per_wg = std::max(1, 2048 / chunks_per_tok);
   return launched(paq::launch_quant_append(a, (hipStream_t)stream), "kv_quant_append");
+}
+
+int32_t paged_attn_decode_host(const paq_desc* d, const float* query, float* out,
+                               const void* key_cache, const void* value_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* cum_q,
+                               const int32_t* past_lens, float softmax_scale,
+                               int32_t num_splits, int32_t num_threads) {
+  SeqStats st;
+  int rc = validate(d, cum_q, past_lens, &st);
+  if (rc) return rc;
+  if (d->q_dtype != PAQ_DT_F32)
+    return fail(PAQ_ERR_UNSUPPORTED, "the host decode takes fp32 queries (q_dtype %d)",
+                d->q_dtype);
+  for (int b = 0; b < d->batch; ++b)
+    if (cum_q[b + 1] - cum_q[b] > 1)
+      return fail(PAQ_ERR_INVALID_ARG, "decode needs q_len 0 or 1 (sequence %d has %d)", b,
+                  cum_q[b + 1] - cum_q[b]);
+  if (num_splits < 0) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d < 0", num_splits);
+  if (d->num_heads / d->kv_num_heads > 64)
+    return fail(PAQ_ERR_UNSUPPORTED, "more than 64 query heads per kv head");
+  if (st.active == 0) return PAQ_OK;
+  if (!query || !out || !key_cache || !value_cache || !k_scale || !v_scale || !block_table)
+    return fail(PAQ_ERR_INVALID_ARG, "a host pointer argument is NULL");
+  paq::HostDecodeArgs a;
+  a.query = query;
+  a.out = out;
+  a.key_cache = (const uint8_t*)key_cache;
+  a.value_cache = (const uint8_t*)value_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.cum_q = cum_q;
+  a.past_lens = past_lens;
+  a.batch = d->batch;
+  a.num_heads = d->num_heads;
+  a.hkv = d->kv_num_heads;
+  a.head_size = d->head_size;
+  a.block_size = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.kv_format = d->kv_format;
+  a.scale_mode = d->scale_mode;
+  a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d->head_size);
+  a.splits = num_splits;
+  a.threads = num_threads > 0 ? num_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  if (paq::host_decode(a)) return fail(PAQ_ERR_UNSUPPORTED, "host decode shape not handled");
+  return PAQ_OK;
 }
 
 int32_t kv_quant_append_rotary(const paq_desc* d, int32_t kv_in_dtype, void* query,

@@ -114,6 +114,34 @@ def counters(workload, kind):
     return int((c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"]) * 1024)
 
 
+def cpu_kernel(w, g, desc, calls=5):
+    """The library's own host decode (paged_attn_decode_host: fp32 GEMV decode,
+    flash decoding across threads) on the whole workload, with the caches the
+    GPU wrote copied to host memory: a fast CPU figure beside the oracle's."""
+    import attention_paged_quantized_amd as paq
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(16, threads))
+    kc, vc = g.kc.cpu().numpy(), g.vc.cpu().numpy()
+    q = np.ascontiguousarray(w.query.float().numpy())
+    out = np.empty_like(q)
+    args = (kc, vc, np.ascontiguousarray(w.k_scale, np.float32),
+            np.ascontiguousarray(w.v_scale, np.float32),
+            np.ascontiguousarray(w.block_table, np.int32), np.ascontiguousarray(w.cum_q, np.int32),
+            np.ascontiguousarray(w.past_lens, np.int32))
+    d32 = paq.make_desc(desc.batch, desc.token_count, desc.num_heads, desc.kv_num_heads,
+                        desc.head_size, desc.block_size, desc.num_blocks,
+                        desc.max_blocks_per_seq, "f32", desc.kv_format, desc.scale_mode)
+    paq.paged_attn_decode_host(d32, q, out, *args, num_threads=threads)       # warm
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        paq.paged_attn_decode_host(d32, q, out, *args, num_threads=threads)
+    sec = (time.perf_counter() - t0) / calls
+    kvb = kv_bytes(w)
+    return {"kernel": "paged_attn_decode_host", "value": round(kvb / sec / 1e9, 2),
+            "unit": "GB/s", "ms_per_call": round(sec * 1e3, 3), "threads": threads,
+            "tokens_per_s": round(int((w.q_lens > 0).sum()) / sec, 1)}
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, on the host cores, over a bounded sample of the
     same workload: its sequences one after another (cycling through the batch)
@@ -533,6 +561,8 @@ def main():
                         "traffic": counters(w.name, "rotary_append_kernel" if args.rotary
                                             else "quant_append_kernel")}
     result["hbm_copy_GBs"] = round(copy_gbs, 1)
+    if kind == "decode" and not args.no_cpu_baseline:
+        result["cpu_kernel"] = cpu_kernel(w, devs[0], desc)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (%.0f s budget)" % args.cpu_seconds,
               file=sys.stderr, flush=True)

@@ -7,7 +7,8 @@
  *                       (kv_quant_append_rotary: rotary embedding first);
  *   paged_attn_decode   GQA decode (one new token per sequence), single pass or
  *                       split-KV ("flash decoding") with a log-sum-exp merge;
- *   paged_attn_prefill  ragged, causal, chunked prefill.
+ *   paged_attn_prefill  ragged, causal, chunked prefill;
+ *   paged_attn_decode_host  the same decode on the host CPU, host-resident data.
  *
  * Problem statement (shared by all three; the cache shape with
  * cache_head_size is from "ONNX Runtime: INT4 Paged KV Cache", section 2; the
@@ -196,6 +197,25 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
                         const int32_t* block_table, const int32_t* cum_q,
                         const int32_t* past_lens, const int32_t* cum_q_host,
                         const int32_t* past_lens_host, void* stream);
+
+/* GQA decode on the host CPU over host-resident caches: the CPU workload of
+ * "GQA GEMV decode" (sections 2-3).  Every pointer is HOST memory (including
+ * block_table, cum_q and past_lens); nothing touches a GPU, and no GPU call
+ * ever falls back to it.  A dedicated M = 1 kernel: each key row is
+ * dequantized once and dotted with the G query heads of its kv head, each
+ * value row accumulated with their softmax weights (fp32 throughout, online
+ * softmax over 256-key tiles).  When active sequences x kv heads is below
+ * num_threads, each sequence's keys are split into block-aligned chunks
+ * (num_splits, 0 = automatic) run on separate threads and merged by their
+ * log-sum-exps.  d->q_dtype must be PAQ_DT_F32 (PAQ_ERR_UNSUPPORTED
+ * otherwise); q_len must be 0 or 1; num_threads 0 = the host's hardware
+ * threads.  Blocks the calling thread until done. */
+int32_t paged_attn_decode_host(const paq_desc* d, const float* query, float* out,
+                               const void* key_cache, const void* value_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* cum_q,
+                               const int32_t* past_lens, float softmax_scale,
+                               int32_t num_splits, int32_t num_threads);
 
 /* kv_quant_append with rotary position embedding (RoPE) of the new rows first,
  * in the same launch.  The step just before attention; "PagedAttention FA
