@@ -26,10 +26,11 @@ Modules
   brute      pure-Python scalar-loop attention for tiny inputs.
   rotary     rotary position embedding of the new rows and the fused
              rotate-then-quantize append.
+  sparse     block-sparse decode over selected KV blocks.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 library special cases, exhaustive enumeration or brute force.  Nothing here is
 "parity unpinned".
 """
 
-from . import codecs, quant, attention, brute, rotary  # noqa: F401
+from . import codecs, quant, attention, brute, rotary, sparse  # noqa: F401

@@ -1,0 +1,45 @@
+"""Block-sparse decode: each new query row attends only to the keys of the
+KV blocks selected for its sequence.  Test infrastructure only (see the
+package docstring).
+
+Source.  "INT8-KV Tensor-Core DynamicSparseAttention" (P2), section 1: a
+decode (and prefill) attention over a dynamically selected subset of an INT8
+KV cache, with a split-K variant.  The page does not give the selection
+rule.  Reading (the plainest): the caller passes, for sequence b, num_sel[b]
+ascending logical block indices sel[b, :num_sel[b]] (each < ceil(kv_len/bs));
+the query row attends to exactly the keys t < kv_len whose block t // bs is
+selected, with the ordinary scaled-dot-product softmax over them.
+"""
+
+import numpy as np
+
+from . import attention
+
+
+def block_sparse_decode(query, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
+                        past_lens, kv_format, sel, num_sel, softmax_scale=None):
+    """query (T, H, D), one row per sequence with a new token; returns float64 (T, H, D)."""
+    q = np.asarray(query, dtype=np.float64)
+    T, H, D = q.shape
+    hkv = key_cache.shape[2]
+    G = H // hkv
+    bs = key_cache.shape[1]
+    sigma = attention.default_scale(D, softmax_scale)
+    out = np.zeros((T, H, D))
+    for b in range(len(past_lens)):
+        r0, r1 = int(cum_q[b]), int(cum_q[b + 1])
+        if r1 == r0:
+            continue
+        if r1 - r0 != 1:
+            raise ValueError("decode: one new row per sequence")
+        L = int(past_lens[b]) + 1
+        K = attention.sequence_kv(key_cache, kv_format, k_scale, block_table[b], L, D)
+        V = attention.sequence_kv(value_cache, kv_format, v_scale, block_table[b], L, D)
+        chosen = set(int(x) for x in sel[b][: int(num_sel[b])])
+        keep = np.array([t // bs in chosen for t in range(L)])
+        for h in range(H):
+            g = h // G
+            s = sigma * (K[keep, g] @ q[r0, h])
+            p = np.exp(s - s.max())
+            out[r0, h] = (p @ V[keep, g]) / p.sum()
+    return out
