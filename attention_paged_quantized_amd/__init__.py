@@ -29,7 +29,8 @@ PATHS = {0: "none", 1: "single", 2: "split", 3: "f32_single", 4: "f32_split", 5:
 EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_decode",
            "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
            "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary",
-           "paged_attn_decode_host")
+           "paged_attn_decode_host", "paged_attn_decode_sparse",
+           "paged_attn_decode_sparse_workspace_size")
 
 
 class PaqDesc(ctypes.Structure):
@@ -85,6 +86,14 @@ def lib():
         L.kv_quant_append.restype = ctypes.c_int32
         L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
                                       _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
+        L.paged_attn_decode_sparse.restype = ctypes.c_int32
+        L.paged_attn_decode_sparse.argtypes = attn[:-1] + [_VP, _VP, _I32P, ctypes.c_int32,
+                                                           ctypes.c_float, ctypes.c_int32, _VP,
+                                                           ctypes.c_size_t, _VP]
+        L.paged_attn_decode_sparse_workspace_size.restype = ctypes.c_size_t
+        L.paged_attn_decode_sparse_workspace_size.argtypes = [ctypes.POINTER(PaqDesc), _I32P,
+                                                              _I32P, _I32P, ctypes.c_int32,
+                                                              ctypes.c_int32]
         L.paged_attn_decode_host.restype = ctypes.c_int32
         L.paged_attn_decode_host.argtypes = [ctypes.POINTER(PaqDesc), _VP, _VP, _VP, _VP, _VP,
                                              _VP, _VP, _VP, _VP, ctypes.c_float,
@@ -254,3 +263,29 @@ def paged_attn_decode_host(desc, query, out, key_cache, value_cache, k_scale, v_
         host(key_cache, np.uint8), host(value_cache, np.uint8), host(k_scale, np.float32),
         host(v_scale, np.float32), host(block_table, np.int32), host(cum_q, np.int32),
         host(past_lens, np.int32), float(softmax_scale), int(num_splits), int(num_threads)))
+
+
+def paged_attn_decode_sparse_workspace_size(desc, cum_q_host, past_lens_host, num_sel_host,
+                                            max_sel, num_splits=0):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    c, pc = _host_i32(num_sel_host)
+    return int(lib().paged_attn_decode_sparse_workspace_size(ctypes.byref(desc), pa, pb, pc,
+                                                             int(max_sel), int(num_splits)))
+
+
+def paged_attn_decode_sparse(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                             block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                             sel_blocks, num_sel, num_sel_host, softmax_scale=0.0, num_splits=0,
+                             workspace=None, stream=None):
+    """Block-sparse decode: sel_blocks (batch, max_sel) and num_sel (batch) are
+    int32 device tensors; num_sel_host their host copy."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    c, pc = _host_i32(num_sel_host)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attn_decode_sparse(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        _dev(sel_blocks), _dev(num_sel), pc, int(sel_blocks.shape[1]), float(softmax_scale),
+        int(num_splits), _dev(workspace), ws_bytes, _stream(stream)))

@@ -107,6 +107,11 @@ int launch_decode_f32(const AttnArgs& a, hipStream_t st);     // any q_len (port
 int launch_decode_mfma(const AttnArgs& a, hipStream_t st);    // q_len in {0,1}
 int launch_combine(const AttnArgs& a, hipStream_t st);
 int launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
+// block-sparse decode: selected blocks -> compact table + effective past
+int launch_sparse_compact(const int32_t* block_table, int max_blocks, const int32_t* sel,
+                          const int32_t* num_sel, int max_sel, const int32_t* cum_q,
+                          const int32_t* past_lens, int block_size, int batch, int32_t* compact,
+                          int32_t* eff_past, hipStream_t st);
 
 // Shape support of the MFMA kernels (host checks before choosing a path).
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype);

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 #include <thread>
 #include <string>
 
@@ -279,6 +280,60 @@ int launched(int launcher_rc, const char* what) {
   return PAQ_OK;
 }
 
+// Decode launch shared by the dense and the block-sparse entry points: the
+// single-pass or split kernel, and the combine after a split.
+int run_decode(const paq_desc* d, const paq_plan& p, paq::AttnArgs& a, void* workspace,
+               hipStream_t st) {
+  int rc;
+  if (p.num_splits > 1) {
+    rc = device_cu_count(&a.num_cus);
+    if (rc) return rc;
+    a.part_count = p.grid_z;
+    const size_t rows = (size_t)d->token_count * d->num_heads * a.part_count;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
+  }
+  if (p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT)
+    rc = launched(paq::launch_decode_mfma(a, st), "decode (MFMA)");
+  else
+    rc = launched(paq::launch_decode_f32(a, st), "decode (fp32)");
+  if (rc) return rc;
+  if (p.num_splits > 1) rc = launched(paq::launch_combine(a, st), "split-KV combine");
+  return rc;
+}
+
+// Block-sparse decode plan: the decode over the compact table of selected
+// blocks (max_sel columns), with every active sequence's key count bounded by
+// num_sel * block_size (the exact count, known on the device, can be smaller
+// only by the unused tail of a selected last block).
+int plan_sparse(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
+                const int32_t* num_sel_host, int max_sel, int num_splits, paq_desc* dc,
+                std::vector<int32_t>* past_c, paq_plan* p) {
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_host, &st);
+  if (rc) return rc;
+  if (max_sel < 1) return fail(PAQ_ERR_INVALID_ARG, "max_sel %d < 1", max_sel);
+  if (d->batch > 0 && !num_sel_host) return fail(PAQ_ERR_INVALID_ARG, "num_sel_host is NULL");
+  *dc = *d;
+  dc->max_blocks_per_seq = max_sel;
+  past_c->assign(d->batch, 0);
+  for (int b = 0; b < d->batch; ++b) {
+    if (cum_q_host[b + 1] == cum_q_host[b]) continue;
+    const int nb = (past_host[b] + 1 + d->block_size - 1) / d->block_size;
+    const int n = num_sel_host[b];
+    if (n < 1 || n > max_sel || n > nb)
+      return fail(PAQ_ERR_INVALID_ARG,
+                  "sequence %d selects %d blocks (needs 1..min(max_sel %d, its %d blocks))", b,
+                  n, max_sel, nb);
+    (*past_c)[b] = n * d->block_size - 1;
+  }
+  return plan_decode(dc, cum_q_host, past_c->data(), num_splits, 0, p);
+}
+
+size_t sparse_head_bytes(int batch, int max_sel) {
+  return align_up((size_t)batch * max_sel * 4) + align_up((size_t)batch * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,22 +397,63 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
   }
   paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
                               block_table, cum_q, past_lens, softmax_scale, p);
-  if (p.num_splits > 1) {
-    rc = device_cu_count(&a.num_cus);
-    if (rc) return rc;
-    a.part_count = p.grid_z;
-    const size_t rows = (size_t)d->token_count * d->num_heads * a.part_count;
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
-  }
-  hipStream_t st = (hipStream_t)stream;
-  if (p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT)
-    rc = launched(paq::launch_decode_mfma(a, st), "decode (MFMA)");
-  else
-    rc = launched(paq::launch_decode_f32(a, st), "decode (fp32)");
+  return run_decode(d, p, a, workspace, (hipStream_t)stream);
+}
+
+// ---- block-sparse decode ----
+
+int32_t paged_attn_decode_sparse(const paq_desc* d, const void* query, void* out,
+                                 const void* key_cache, const void* value_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* cum_q,
+                                 const int32_t* past_lens, const int32_t* cum_q_host,
+                                 const int32_t* past_lens_host, const int32_t* sel_blocks,
+                                 const int32_t* num_sel, const int32_t* num_sel_host,
+                                 int32_t max_sel, float softmax_scale, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  paq_desc dc;
+  std::vector<int32_t> past_c;
+  paq_plan p;
+  int rc = plan_sparse(d, cum_q_host, past_lens_host, num_sel_host, max_sel, num_splits, &dc,
+                       &past_c, &p);
   if (rc) return rc;
-  if (p.num_splits > 1) rc = launched(paq::launch_combine(a, st), "split-KV combine");
-  return rc;
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  if (!sel_blocks || !num_sel) return fail(PAQ_ERR_INVALID_ARG, "sel_blocks / num_sel is NULL");
+  const size_t head = sparse_head_bytes(d->batch, max_sel);
+  if (!workspace || workspace_bytes < head + p.workspace_bytes)
+    return fail(PAQ_ERR_WORKSPACE, "sparse decode needs %llu workspace bytes, got %llu",
+                (unsigned long long)(head + p.workspace_bytes),
+                (unsigned long long)workspace_bytes);
+  if (((uintptr_t)workspace) % 16)
+    return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int32_t* compact = (int32_t*)workspace;
+  int32_t* eff_past = (int32_t*)((char*)workspace + align_up((size_t)d->batch * max_sel * 4));
+  hipStream_t st = (hipStream_t)stream;
+  rc = launched(paq::launch_sparse_compact(block_table, d->max_blocks_per_seq, sel_blocks,
+                                           num_sel, max_sel, cum_q, past_lens, d->block_size,
+                                           d->batch, compact, eff_past, st),
+                "sparse block selection");
+  if (rc) return rc;
+  paq::AttnArgs a = attn_args(&dc, query, out, key_cache, value_cache, k_scale, v_scale,
+                              compact, cum_q, eff_past, softmax_scale, p);
+  return run_decode(&dc, p, a, (char*)workspace + head, st);
+}
+
+size_t paged_attn_decode_sparse_workspace_size(const paq_desc* d, const int32_t* cum_q_host,
+                                               const int32_t* past_lens_host,
+                                               const int32_t* num_sel_host, int32_t max_sel,
+                                               int32_t num_splits) {
+  paq_desc dc;
+  std::vector<int32_t> past_c;
+  paq_plan p;
+  if (plan_sparse(d, cum_q_host, past_lens_host, num_sel_host, max_sel, num_splits, &dc,
+                  &past_c, &p))
+    return 0;
+  if (p.path == PAQ_PATH_NONE) return 0;
+  return sparse_head_bytes(d->batch, max_sel) + p.workspace_bytes;
 }
 
 int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,

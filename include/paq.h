@@ -8,6 +8,7 @@
  *   paged_attn_decode   GQA decode (one new token per sequence), single pass or
  *                       split-KV ("flash decoding") with a log-sum-exp merge;
  *   paged_attn_prefill  ragged, causal, chunked prefill;
+ *   paged_attn_decode_sparse  decode over caller-selected KV blocks;
  *   paged_attn_decode_host  the same decode on the host CPU, host-resident data.
  *
  * Problem statement (shared by all three; the cache shape with
@@ -197,6 +198,39 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
                         const int32_t* block_table, const int32_t* cum_q,
                         const int32_t* past_lens, const int32_t* cum_q_host,
                         const int32_t* past_lens_host, void* stream);
+
+/* Block-sparse GQA decode ("INT8-KV Tensor-Core DynamicSparseAttention",
+ * section 1; the page gives no selection rule, so the selection is an input):
+ * the new token of sequence b attends to exactly the keys t < kv_len_b whose
+ * logical block t / block_size is one of sel_blocks[b][0 .. num_sel[b]).
+ *   sel_blocks   int32 (batch, max_sel), device: ascending logical block
+ *                indices, each < ceil(kv_len_b / block_size) (not checked:
+ *                device data, like block ids)
+ *   num_sel      int32 (batch), device; num_sel_host its host copy, each in
+ *                [1, min(max_sel, ceil(kv_len_b / block_size))] for sequences
+ *                with a new row (checked on the host)
+ * Runs a small kernel that turns the selection into a compact block table
+ * and effective key counts, then the dense decode kernels over it (single
+ * pass or split-KV with num_splits as for paged_attn_decode, planned on
+ * num_sel_host * block_size keys).  `workspace` (device, 16-byte aligned)
+ * must hold paged_attn_decode_sparse_workspace_size() bytes; it is
+ * overwritten.  Otherwise as paged_attn_decode. */
+int32_t paged_attn_decode_sparse(const paq_desc* d, const void* query, void* out,
+                                 const void* key_cache, const void* value_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_table, const int32_t* cum_q,
+                                 const int32_t* past_lens, const int32_t* cum_q_host,
+                                 const int32_t* past_lens_host, const int32_t* sel_blocks,
+                                 const int32_t* num_sel, const int32_t* num_sel_host,
+                                 int32_t max_sel, float softmax_scale, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of paged_attn_decode_sparse (0 when the arguments are
+ * invalid or there is nothing to do). */
+size_t paged_attn_decode_sparse_workspace_size(const paq_desc* d, const int32_t* cum_q_host,
+                                               const int32_t* past_lens_host,
+                                               const int32_t* num_sel_host, int32_t max_sel,
+                                               int32_t num_splits);
 
 /* GQA decode on the host CPU over host-resident caches: the CPU workload of
  * "GQA GEMV decode" (sections 2-3).  Every pointer is HOST memory (including

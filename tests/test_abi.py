@@ -231,3 +231,24 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         paq.paged_attn_prefill(d, x, x, x, x, x, x, x, x, x, [0, 1], [0], stream=0)
+
+
+def test_sparse_decode_checks():
+    L = paq.lib()
+    d = _desc(2, 2)
+    cum, past = [0, 1, 2], [40, 9]                    # 41 and 10 keys: 3 and 1 blocks of 16
+    assert paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [2, 1], 3, 1) > 0
+    assert paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [4, 1], 4, 1) == 0  # > 3 blocks
+    assert paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [0, 1], 3, 1) == 0  # none
+    assert paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [2, 1], 1, 1) == 0  # > max_sel
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    c, pc = paq._host_i32([2, 2])                    # sequence 1 has only one block
+    rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, 1, FAKE, 1 << 20,
+                                    None)
+    assert rc == paq.PAQ_ERR_INVALID_ARG and "selects 2 blocks" in paq.paq_last_error()
+    c, pc = paq._host_i32([2, 1])
+    rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, 1, FAKE, 16, None)
+    assert rc == paq.PAQ_ERR_WORKSPACE
