@@ -62,6 +62,10 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then "
                          "WRITE_SIZE) into profiles/counters_<workload>.json and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--sparse", action="store_true",
+                    help="decode: block-sparse attention over a local window of 2 blocks plus "
+                         "every 3rd earlier block (paged_attn_decode_sparse); value counts the "
+                         "selected KV bytes")
     ap.add_argument("--rotary", action="store_true",
                     help="the step's append is kv_quant_append_rotary (rotary embedding of "
                          "the new query and key rows over all head_size channels)")
@@ -395,9 +399,29 @@ def main():
         if nbytes:
             ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.sparse:
+        if kind != "decode":
+            sys.exit("--sparse applies to decode workloads")
+        nbk = -(-(w.past_lens + 1) // w.block_size)
+        rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in nbk]
+        sel_np = np.zeros((w.batch, max(len(r) for r in rows)), np.int32)
+        num_np = np.array([len(r) for r in rows], np.int32)
+        for b, r in enumerate(rows):
+            sel_np[b, :len(r)] = r
+        sel_d, num_d = torch.from_numpy(sel_np).to(dev), torch.from_numpy(num_np).to(dev)
+        nbytes = paq.paged_attn_decode_sparse_workspace_size(desc, w.cum_q, w.past_lens, num_np,
+                                                             sel_np.shape[1], S)
+        ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=dev)
+        # selected keys: whole blocks, the last one up to kv_len
+        sel_keys = [sum(min(w.block_size, int(w.past_lens[b]) + 1 - w.block_size * x) for x in r)
+                    for b, r in enumerate(rows)]
 
     def attention(g, out):
-        if kind == "decode":
+        if kind == "decode" and args.sparse:
+            paq.paged_attn_decode_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                         g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
+                                         sel_d, num_d, num_np, 0.0, S, ws, stream)
+        elif kind == "decode":
             paq.paged_attn_decode(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                   g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0, S,
                                   ws, stream)
@@ -519,6 +543,10 @@ def main():
            "q_dtype": w.q_dtype, "token_count": T, "kv_pools": pools}
     if kind == "decode":
         kvb = kv_bytes(w)
+        if args.sparse:
+            act = w.q_lens > 0
+            kvb = int(sum(k for k, a in zip(sel_keys, act) if a)) * w.kv_num_heads * 2 * \
+                w.cache_head_size
         act = int((w.q_lens > 0).sum())
         result.update({"value": round(kvb / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s",
                        "tokens_per_s": round(act / (ms_step / 1e3), 1),
@@ -526,11 +554,12 @@ def main():
         cfg.update({"num_splits": S, "kv_bytes_per_step": kvb,
                     "max_kv_len": int(w.kv_lens.max())})
         achieved = kvb / (kern_avg / 1e3) / 1e9
-        traffic = counters(w.name, "decode")
+        traffic = None if args.sparse else counters(w.name, "decode")
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                              "kernel": "paged_attn_decode call (%s)" %
+                              "kernel": ("paged_attn_decode_sparse call (sparse_compact_kernel + %s)"
+                                         if args.sparse else "paged_attn_decode call (%s)") %
                                         ("decode_stream_kernel" + (" + combine_kernel" if S > 1 else "")),
                               "kernel_us_avg": round(kern_avg * 1e3, 3),
                               "kernel_us_p10_p90": [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
@@ -561,7 +590,10 @@ def main():
                         "traffic": counters(w.name, "rotary_append_kernel" if args.rotary
                                             else "quant_append_kernel")}
     result["hbm_copy_GBs"] = round(copy_gbs, 1)
-    if kind == "decode" and not args.no_cpu_baseline:
+    if args.sparse:
+        cfg["sparse"] = "2-block local window + every 3rd earlier block; %d of %d KV bytes" % (
+            kvb, kv_bytes(w))
+    if kind == "decode" and not args.no_cpu_baseline and not args.sparse:
         result["cpu_kernel"] = cpu_kernel(w, devs[0], desc)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (%.0f s budget)" % args.cpu_seconds,
