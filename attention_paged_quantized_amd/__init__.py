@@ -23,14 +23,15 @@ DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 KV_FORMATS = {"int8": 0, "int4": 1, "fp8": 2}
 SCALE_MODES = {"channel": 0, "head": 1}
 PATHS = {0: "none", 1: "single", 2: "split", 3: "f32_single", 4: "f32_split", 5: "prefill",
-         6: "f32_prefill"}
+         6: "f32_prefill", 7: "balanced"}
+ABI_VERSION = 2
 
 # Every symbol include/paq.h declares.
 EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_decode",
            "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
            "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary",
            "paged_attn_decode_host", "paged_attn_decode_sparse",
-           "paged_attn_decode_sparse_workspace_size")
+           "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded")
 
 
 class PaqDesc(ctypes.Structure):
@@ -42,7 +43,9 @@ class PaqDesc(ctypes.Structure):
 class PaqPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "max_query_len", "max_kv_len", "active_seqs", "work_units", "num_splits", "path",
-        "grid_x", "grid_y", "grid_z", "reserved")] + [("workspace_bytes", ctypes.c_uint64)]
+        "grid_x", "grid_y", "grid_z", "waves_per_group", "parts", "parts_per_seq",
+        "chunks_per_part", "keys_per_group")] + [
+        ("total_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class PaqError(RuntimeError):
@@ -83,6 +86,8 @@ def lib():
         L.paged_attn_decode.argtypes = attn + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
         L.paged_attn_prefill.restype = ctypes.c_int32
         L.paged_attn_prefill.argtypes = attn + [_VP]
+        L.paged_attn_prefill_padded.restype = ctypes.c_int32
+        L.paged_attn_prefill_padded.argtypes = attn + [ctypes.c_int32, _VP]
         L.kv_quant_append.restype = ctypes.c_int32
         L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
                                       _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
@@ -212,6 +217,19 @@ def paged_attn_prefill(desc, query, out, key_cache, value_cache, k_scale, v_scal
         ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         float(softmax_scale), _stream(stream)))
+
+
+def paged_attn_prefill_padded(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                              max_query_len, softmax_scale=0.0, stream=None):
+    """paged_attn_prefill with the grid sized from max_query_len (>= the exact
+    maximum) for every (sequence, kv head) pair."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    _check(lib().paged_attn_prefill_padded(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        float(softmax_scale), int(max_query_len), _stream(stream)))
 
 
 def kv_quant_append(desc, kv_in_dtype, key, value, key_cache, value_cache, k_scale, v_scale,

@@ -10,15 +10,18 @@
 // output ("GQA GEMV decode", section 2: flash decoding partials).
 //
 // Keys are processed 256 at a time, one per thread for the scores (online
-// softmax across chunks, exact exp), then every thread owns one channel of one
-// key slice for the probability-weighted value sum.
+// softmax across chunks), then every thread owns one channel of one key slice
+// for the probability-weighted value sum.  Scores stay in raw units (query
+// times key scale over its power-of-two normaliser, dotted with the codes);
+// exponents are formed as (raw - raw max) * factor, so key scales anywhere in
+// the finite fp32 range neither overflow nor produce a NaN.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace paq {
 
 constexpr int kF32Threads = 256;
-constexpr int kF32MaxGroup = 16;
+constexpr int kF32MaxGroup = kF32KernelMaxGroup;
 constexpr int kF32MaxD = 128;
 
 template <int KVF>
@@ -87,12 +90,18 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   __shared__ float qs[kF32MaxGroup][kF32MaxD];
   __shared__ float sc[kF32MaxGroup][kF32Threads];
   __shared__ float m_sh[kF32MaxGroup], l_sh[kF32MaxGroup], alpha_sh[kF32MaxGroup];
+  __shared__ int e_sh;
 
+  // q' = q * s / M with M = 2^e >= max|s| of this kv head (exact scaling; M
+  // finite for every finite scale): raw scores q'.codes never overflow, and
+  // the score factor c2 = softmax_scale * M * log2(e) is kept finite
+  const int e = key_scale_exponent<SM>(a.k_scale, g, D, &e_sh);
+  const float c2 = score_factor_log2(a.softmax_scale, e, 1.f);
   const TQ* q = reinterpret_cast<const TQ*>(a.query);
-  for (int e = tid; e < G * D; e += kF32Threads) {
-    const int hh = e / D, d = e % D;
+  for (int i = tid; i < G * D; i += kF32Threads) {
+    const int hh = i / D, d = i % D;
     const float s = (SM == SCALE_CHANNEL) ? a.k_scale[g * D + d] : a.k_scale[g];
-    qs[hh][d] = to_f32(q[((size_t)r * H + g * G + hh) * D + d]) * s;
+    qs[hh][d] = to_f32(q[((size_t)r * H + g * G + hh) * D + d]) * ldexpf(s, -e);
   }
   if (tid < G) { m_sh[tid] = -INFINITY; l_sh[tid] = 0.f; }
 
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int hh = 0; hh < kF32MaxGroup; ++hh)
-      if (hh < G) sc[hh][tid] = (j < kend) ? dot[hh] * a.softmax_scale : -INFINITY;
+      if (hh < G) sc[hh][tid] = (j < kend) ? dot[hh] : -INFINITY;   // raw scores
     __syncthreads();
     // per-head chunk maximum -> new running max and rescale factor
     for (int hh = wave; hh < G; hh += kF32Threads / 64) {
@@ -140,14 +149,14 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       if (lane == 0) {
         const float m_old = m_sh[hh];
         const float m_new = fmaxf(m_old, mx);
-        alpha_sh[hh] = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
+        alpha_sh[hh] = (m_old == -INFINITY) ? 0.f : exp2f((m_old - m_new) * c2);
         m_sh[hh] = m_new;
       }
     }
     __syncthreads();
     for (int hh = 0; hh < G; ++hh) {
       const float v = sc[hh][tid];
-      sc[hh][tid] = (v == -INFINITY) ? 0.f : expf(v - m_sh[hh]);
+      sc[hh][tid] = (v == -INFINITY) ? 0.f : exp2f((v - m_sh[hh]) * c2);
     }
     __syncthreads();
     for (int hh = wave; hh < G; hh += kF32Threads / 64) {
@@ -203,10 +212,16 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       TQ* out = reinterpret_cast<TQ*>(a.out);
       out[((size_t)r * H + h) * D + my_d] = from_f32<TQ>(o * vs);
     } else {
-      // split-KV partials leave the value scale to the combine
+      // split-KV partials leave the value scale to the combine; the chunk's
+      // log-sum-exp is kept as the pair (raw maximum, log2 of the sum), which
+      // cannot overflow at any score factor (the combine scales differences
+      // of raw maxima by c2)
       const size_t pi = ((size_t)r * H + h) * S + chunk;
       a.part_o[pi * D + my_d] = o;
-      if (my_d == 0) a.part_lse[pi] = (l > 0.f) ? m_sh[hh] + logf(l) : -INFINITY;
+      if (my_d == 0) {
+        a.part_lse[2 * pi] = (l > 0.f) ? m_sh[hh] : -INFINITY;
+        a.part_lse[2 * pi + 1] = (l > 0.f) ? log2f(l) : -INFINITY;
+      }
     }
   }
 }

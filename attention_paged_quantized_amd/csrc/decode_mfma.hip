@@ -1,12 +1,10 @@
 // decode_mfma.hip -- GQA paged decode over an INT8 / packed-INT4 / FP8 cache on
 // gfx950 matrix cores (v_mfma_f32_16x16x32_f16), single pass or split-KV.
 //
-// Work unit: a wave streams the 32-key tiles of a key range for HW adjacent kv
+// Work unit: a wave streams 32-key tiles of a key range for HW adjacent kv
 // heads (HW = 128 / row bytes, so every copied row segment is a whole 128-byte
-// line) with its own online softmax.  Single pass: the 8 waves of a
-// workgroup share one (sequence, head group) and merge through LDS at the end;
-// split-KV: each wave owns one chunk, and the workgroup merges its chunks
-// through LDS and writes one partial for the combine.
+// line) with its own online softmax; the 8 waves of a workgroup take the
+// tiles of a key range in turn and merge through LDS at its end.
 // Decode is HBM-bound (every K/V byte is read once -- "GQA GEMV decode",
 // why-it-is-good item 1), so the design streams the raw codes HBM -> LDS with
 // whole-line non-temporal DMA copies, reads each lane's operand bytes from
@@ -31,10 +29,10 @@
 //   score scale).  The running maximum is refreshed lazily: only when a score
 //   exceeds it by more than 2^8 are the maxima exchanged and the accumulators
 //   rescaled, so P stays <= 2^15, inside fp16 range.
-// * Split-KV ("flash decoding", "GQA GEMV decode" section 2): chunk c covers
-//   blocks [c*nb/S, (c+1)*nb/S) of the sequence; each workgroup writes the
-//   normalised partial output of its chunks and its log-sum-exp for the
-//   combine kernel.
+// * Split-KV ("flash decoding", "GQA GEMV decode" section 2), in two forms:
+//   block-aligned chunks per sequence, or an equal share of all tiles per
+//   workgroup (see the partition below); partial results are merged by the
+//   last workgroup of a sequence to finish, inside the same launch.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -327,9 +325,10 @@ __device__ __forceinline__ void read_tile(const uint8_t* slot, TileRaw<KVF, D>& 
   }
 }
 
-// Per-wave online-softmax state: running max (log2 units), this lane's share of
-// the running sum, and the O^T accumulators (lane j+16q: query column j,
-// channels (D/16)*(4q+r) + nb).
+// Per-wave online-softmax state: running maximum of the raw scores (the
+// MFMA outputs, before the score factor), this lane's share of the running
+// sum, and the O^T accumulators (lane j+16q: query column j, channels
+// (D/16)*(4q+r) + nb).
 template <int D> struct WaveState {
   float m = -INFINITY, l = 0.f;
   f32x4 o[D / 16];
@@ -352,7 +351,7 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0op, qlo[m], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1op, qlo[m], s1, 0, 0, 0);
   }
-  // mask keys past the chunk (raw scores; c2 > 0 so maxima commute with it)
+  // mask keys past the range (raw scores; c2 > 0 so maxima commute with it)
   float v[8];
   float lm = -INFINITY;
 #pragma unroll
@@ -369,30 +368,31 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KVF, D>& t, int k0, i
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) lm = fmaxf(lm, v[i]);
-  lm *= c2;
   // The reference maximum of a column is shared by its four lane rows and only
   // moves when a score exceeds it by more than kMaxSlack (log2 units): then the
   // rows exchange their maxima and the accumulators are rescaled.  Otherwise
-  // p = 2^(s - m) <= 2^kMaxSlack, which the 2^7-scaled fp16 P holds.  (The
-  // difference is exact near m, where m + kMaxSlack might round up.)
-  if (__ballot(lm - st.m > kMaxSlack)) {
+  // p = 2^(c2 (s - m)) <= 2^kMaxSlack, which the 2^7-scaled fp16 P holds.  The
+  // gap is formed on the raw scores and scaled afterwards, so it cannot
+  // overflow whatever the factor.
+  if (__ballot((lm - st.m) * c2 > kMaxSlack)) {
     const float m_new = fmaxf(st.m, rows_max(lm));
-    const float alpha = fast_exp2(st.m - m_new);         // 0 on the first update
+    const float alpha = fast_exp2((st.m - m_new) * c2);  // 0 on the first update
     st.m = m_new;
     st.l *= alpha;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) st.o[i] *= alpha;
   }
-  // P' = 2^7 * 2^(s*c2 - m) in fp16; the running sum adds exactly those fp16
+  // P' = 2^7 * 2^(c2 (s - m)) in fp16; the running sum adds exactly those fp16
   // values (two per dot), which the value unbiasing in the epilogue relies on
-  const float bias = kPScaleLog2 - st.m;
+  const float mlog = st.m * c2;
   f16x8 pop;
-  if (__builtin_expect(__ballot(fabsf(st.m) > kHugeScoreLog2) == 0, 1)) {
+  if (__builtin_expect(__ballot(!(fabsf(mlog) <= kHugeScoreLog2)) == 0, 1)) {
+    const float bias = kPScaleLog2 - mlog;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(fmaf(v[i], c2, bias));
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(huge_score_arg(v[i], c2, st.m, kPScaleLog2));
+    for (int i = 0; i < 8; ++i) pop[i] = (f16)fast_exp2(safe_score_arg(v[i], st.m, c2, kPScaleLog2));
   }
   const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
   float l0 = __builtin_amdgcn_fdot2((f16x2){pop[0], pop[1]}, ones, st.l, false);
@@ -440,12 +440,14 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int h, int q0, int
   }
 }
 
-// Fold the key scale into the query: Q' = Q * s / M_h with M_h the power of
-// two >= max|s| of kv head h, split into fp16 hi + lo parts in the QK B-operand
-// layout (lane col+16*grp: query column col, channels of segment grp).
+// Fold the key scale into the query: Q' = Q * s / M_h with M_h = 2^e the power
+// of two >= max|s| of kv head h (scale_exponent: finite for every finite
+// scale), split into fp16 hi + lo parts in the QK B-operand layout (lane
+// col+16*grp: query column col, channels of segment grp).  s / M_h is formed
+// as ldexp(s, -e), exact also for subnormal scales.  Returns e.
 template <int D, int KVF, int SM, typename TQ>
-__device__ __forceinline__ void fold_loaded_query(const QueryRaw<D, SM>& r, f16x8 (&qhi)[D / 32],
-                                                  f16x8 (&qlo)[D / 32], float& Mh) {
+__device__ __forceinline__ int fold_loaded_query(const QueryRaw<D, SM>& r, f16x8 (&qhi)[D / 32],
+                                                 f16x8 (&qlo)[D / 32]) {
   constexpr int NQK = D / 32;
   constexpr int SEG = D / 4;
   float sv[SEG];
@@ -465,220 +467,418 @@ __device__ __forceinline__ void fold_loaded_query(const QueryRaw<D, SM>& r, f16x
 #pragma unroll
     for (int i = 0; i < SEG; ++i) sv[i] = r.s[0][0];
   }
-  int ex;
-  const float fr = frexpf(smax, &ex);                      // smax = fr * 2^ex, fr in [0.5,1)
-  Mh = (smax == 0.f) ? 1.f : ldexpf(1.f, fr == 0.5f ? ex - 1 : ex);
-  const float invM = 1.f / Mh;                             // exact (power of two)
+  const int e = scale_exponent(smax);
   float qv[SEG];
 #pragma unroll
   for (int i = 0; i < SEG / 8; ++i) {
-    const TQ* e = reinterpret_cast<const TQ*>(&r.q[i]);
+    const TQ* x = reinterpret_cast<const TQ*>(&r.q[i]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qv[8 * i + j] = to_f32(e[j]);
+    for (int j = 0; j < 8; ++j) qv[8 * i + j] = to_f32(x[j]);
   }
 #pragma unroll
   for (int m = 0; m < NQK; ++m) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = qk_channel<KVF, D>(0, m, e);          // channel within the segment
-      const float x = qv[c] * (sv[c] * invM);
+    for (int k = 0; k < 8; ++k) {
+      const int c = qk_channel<KVF, D>(0, m, k);          // channel within the segment
+      const float x = qv[c] * ldexpf(sv[c], -e);
       const f16 hi = (f16)x;
-      qhi[m][e] = hi;
-      qlo[m][e] = (f16)(x - (float)hi);
+      qhi[m][k] = hi;
+      qlo[m][k] = (f16)(x - (float)hi);
     }
   }
+  return e;
 }
 
-template <int D, int KVF, int SM, typename TQ>
-__device__ __forceinline__ void fold_query(const AttnArgs& a, int h, int q0, int G, int col,
-                                           int grp, f16x8 (&qhi)[D / 32], f16x8 (&qlo)[D / 32],
-                                           float& Mh) {
-  QueryRaw<D, SM> r;
-  load_query<D, SM, TQ>(a, h, q0, G, col, grp, r);
-  fold_loaded_query<D, KVF, SM, TQ>(r, qhi, qlo, Mh);
+// ---------------------------------------------------------------------------
+// Partition of the keys over workgroups.  A segment is the key range of one
+// (sequence, head group) pair; a piece is a contiguous run of a segment's
+// 32-key tiles that one workgroup streams, its NW waves taking the tiles in
+// turn.  Three partitions (the host plan picks one):
+//   DEC_SINGLE  one workgroup per segment (single pass);
+//   DEC_CHUNKS  S block-aligned chunks per sequence (chunk c = blocks
+//               [c*nb/S, (c+1)*nb/S), "GQA GEMV decode", section 2), CPW
+//               consecutive chunks per workgroup;
+//   DEC_STREAM  the tiles of all segments, concatenated (sequence-major, head
+//               group next), cut into N equal runs, one per workgroup: every
+//               workgroup streams the same bytes whatever the lengths, and a
+//               long sequence is spread over as many compute units as it
+//               needs.  A workgroup's run covers whole segments (written
+//               directly) and at most two partial pieces, its first and its
+//               last.
+// A piece that is a whole segment writes its output directly.  Otherwise it
+// writes a normalised partial (raw maximum, sum, output) and counts its
+// arrival; the last piece of the segment to arrive merges them all by their
+// maxima and writes the output -- in the same launch.
+// ---------------------------------------------------------------------------
+
+// Where a stream-partition workgroup starts: the sequence holding global tile
+// g (a wave-wide prefix sum of HG * tiles_b over the sequences with a new row,
+// 64 sequences at a time), with its offsets.  Not inlined: it runs once per
+// workgroup and, kept apart, leaves the streaming loop's registers alone.
+struct StreamPos {
+  int b;        // sequence (-1: past the last tile)
+  int off;      // g - first global tile of sequence b
+  int tiles;    // 32-key tiles of sequence b
+  int q0, past;
+};
+__device__ __attribute__((noinline)) StreamPos stream_find(const int32_t* __restrict__ cum_q,
+                                                          const int32_t* __restrict__ past,
+                                                          int batch, int hgs, long long g) {
+  const int lane = (int)(threadIdx.x & 63);
+  long long before = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    int tiles = 0, q0 = 0, ps = 0;
+    if (b < batch) {
+      q0 = cum_q[b];
+      ps = past[b];
+      if (cum_q[b + 1] > q0) tiles = (ps + 32) >> 5;       // ceil((past + 1) / 32)
+    }
+    long long incl = (long long)tiles * hgs;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const unsigned long long hit = __ballot(before + incl > g);
+    if (hit) {
+      const int l = (int)__builtin_ctzll(hit);
+      const long long incl_l = __shfl(incl, l, 64);
+      const int tiles_l = __shfl(tiles, l, 64);
+      return StreamPos{b0 + l, (int)(g - (before + incl_l - (long long)tiles_l * hgs)), tiles_l,
+                       __shfl(q0, l, 64), __shfl(ps, l, 64)};
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  return StreamPos{-1, 0, 0, 0, 0};
 }
 
-// Key range of chunk c: blocks [c*nb/S, (c+1)*nb/S) of the sequence.
-// (c * nb stays below 2^32: the host bounds max_blocks_per_seq * num_splits.)
-__device__ __forceinline__ void chunk_keys(int c, int nb, int S, int bs, int kv_len, int& kb,
-                                           int& ke) {
-  kb = (int)(((uint32_t)c * (uint32_t)nb) / (uint32_t)S) * bs;
-  ke = min(kv_len, (int)(((uint32_t)(c + 1) * (uint32_t)nb) / (uint32_t)S) * bs);
+// The stream-partition workgroup whose run holds global tile g: the largest
+// w with floor(w * T / N) <= g.
+__device__ __forceinline__ int stream_owner(long long g, long long T, int N) {
+  return (int)(((g + 1) * (long long)N - 1) / T);
 }
 
-// Decode over one group of HW adjacent kv heads (blockIdx.x) of sequence
-// blockIdx.y.
-//  * Single pass (SPLIT false): the NW waves of the workgroup take the 32-key
-//    tiles of the whole sequence in turn, each with its own online softmax,
-//    and merge through LDS at the end.
-//  * Split-KV (SPLIT true): wave w of workgroup z takes chunk z * NW + w
-//    (blocks [c*nb/S, (c+1)*nb/S), "GQA GEMV decode", section 2).  The waves
-//    never wait for each other while streaming; at the end they merge their
-//    chunks through LDS as in single pass, and the workgroup writes one
-//    partial output for its NW chunks -- normalised, value scale not yet
-//    applied; the combine applies it once -- and its log-sum-exp.
-template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, bool SPLIT>
+// Key range [k0, k1) of part j of a sequence of kv_len keys, chunk partition.
+__device__ __forceinline__ void chunk_part_keys(const AttnArgs& a, int j, int kv_len, int& k0,
+                                                int& k1) {
+  const uint64_t nb = (uint64_t)((kv_len + a.block_size - 1) >> a.block_size_log2);
+  const uint64_t S = (uint64_t)a.num_splits;
+  const uint64_t c0 = (uint64_t)j * a.dec_chunks_per_part;
+  const uint64_t c1 = min(S, c0 + (uint64_t)a.dec_chunks_per_part);
+  k0 = (int)((c0 * nb / S) << a.block_size_log2);
+  k1 = min(kv_len, (int)((c1 * nb / S) << a.block_size_log2));
+}
+
+// Decode: every workgroup streams one piece (single, chunks) or a run of
+// pieces (stream) for one head group of HW adjacent kv heads; the NW waves
+// take the 32-key tiles of a piece in turn, each with its own online softmax,
+// and merge through LDS at the end of the piece.
+template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, int MODE>
 __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
   using Geo = KvGeom<KVF, D>;
   using SG = StreamGeo<KVF, D, HW>;
-  constexpr int NQK = Geo::NQK, NPV = Geo::NPV;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  const int lbs = a.block_size_log2;
-  const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
-  // This wave's key range [kb, ke) and tile stride for a sequence of kv_len
-  // keys.
-  auto wave_range = [&](int kv_len, int& kb, int& ke) {
-    if constexpr (SPLIT) {
-      const int chunk = blockIdx.z * NW + wave;
-      const int nb = (kv_len + a.block_size - 1) >> lbs;
-      if (chunk < a.num_splits) {
-        chunk_keys(chunk, nb, a.num_splits, a.block_size, kv_len, kb, ke);
-      } else {
-        kb = ke = 0;                                      // past the last chunk: empty
-      }
-    } else {
-      kb = 32 * wave;
-      ke = kv_len;
-    }
-  };
-  // The first tile's block ids are read before this sequence's length
-  // arrives, for the batch's longest length (inside the table row either
-  // way); they serve whenever the true range names the same table entries,
-  // which saves the table round trip before the first copy.
   using WC = WaveCopy<KVF, D, HW>;
-  int kb_s, ke_s;
-  wave_range(a.max_kv_len, kb_s, ke_s);
-  const typename WC::Blocks spec = WC::blocks(kb_s, ke_s, lbs, table);
-  const int q0 = a.cum_q[b];
-  const int past = a.past_lens[b];
-  // no new token: no rows.  The test also reads the past and the speculative
-  // entries (a negative past never occurs), so all these loads go out
-  // together instead of one behind the other.
-  if ((a.cum_q[b + 1] == q0) | ((past < 0) & (spec.b0 == spec.b1))) return;
-  const int kv_len = past + 1;
-  const int hkv = a.hkv, H = a.num_heads;
-  const int G = H / hkv;
+  constexpr int NQK = Geo::NQK, NPV = Geo::NPV;
+  constexpr int stride = 32 * NW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
+  const int hgs = a.dec_head_groups;
+  const int lbs = a.block_size_log2;
+  const int hkv = a.hkv, H = a.num_heads;
+  const int G = H / hkv;
   const uint32_t row_stride = (uint32_t)(hkv * Geo::C);   // bytes between tokens
-  const uint8_t* kbase = a.key_cache + (size_t)blockIdx.x * SG::RB;
-  const uint8_t* vbase = a.value_cache + (size_t)blockIdx.x * SG::RB;
-
-  int kb, ke;
-  wave_range(kv_len, kb, ke);
-  const int stride = SPLIT ? 32 : 32 * NW;
-  const bool spec_ok = WC::entry(kb, ke, lbs, 0) == WC::entry(kb_s, ke_s, lbs, 0) &&
-                       WC::entry(kb, ke, lbs, 1) == WC::entry(kb_s, ke_s, lbs, 1);
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NS * SG::SLOT];
+  __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];        // running max, sum per wave
+  __shared__ float sm_c2[HW];
+  __shared__ int sm_last;
   uint8_t* myring = ring[wave];
   WC cp;
   cp.init(lane, row_stride);
 
-  // query and key-scale loads go out first, then this wave's first NS tiles
-  QueryRaw<D, SM> qraw[HW];
-#pragma unroll
-  for (int hh = 0; hh < HW; ++hh)
-    load_query<D, SM, TQ>(a, blockIdx.x * HW + hh, q0, G, col, grp, qraw[hh]);
-  if (kb < ke)
-    cp.issue(myring, kb, ke, lbs, spec_ok ? spec : WC::blocks(kb, ke, lbs, table), kbase, vbase,
-             row_stride);
-#pragma unroll
-  for (int j = 1; j < NS; ++j)
-    if (kb + j * stride < ke)
-      cp.issue(myring + j * SG::SLOT, kb + j * stride, ke, lbs, table, kbase, vbase, row_stride);
-  // The waits below count NS - 1 tiles in flight behind the current one; with
-  // fewer tiles than that, wait for everything instead.
-  if (kb + (NS - 1) * stride >= ke) wait_vmcnt_le<0>();
-
-  f16x8 qhi[HW][NQK], qlo[HW][NQK];
-  float c2[HW];
-#pragma unroll
-  for (int hh = 0; hh < HW; ++hh) {
-    float Mh;
-    fold_loaded_query<D, KVF, SM, TQ>(qraw[hh], qhi[hh], qlo[hh], Mh);
-    c2[hh] = a.softmax_scale * Mh * kLog2e / kKeyOperandScale<KVF>;   // score -> log2 units
-  }
-
-  WaveState<D> st[HW];
-#pragma unroll
-  for (int hh = 0; hh < HW; ++hh)
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) st[hh].o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  int cur = 0;
-  // block ids of the next tile to issue, fetched one iteration ahead
-  typename WaveCopy<KVF, D, HW>::Blocks nb_next =
-      WaveCopy<KVF, D, HW>::blocks(kb + NS * stride, ke, lbs, table);
-  for (int k = kb; k < ke; k += stride) {
-    // this tile's copies are done once at most the later tiles' remain
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_le<(NS - 1) * 2 * SG::NI>();
-    __builtin_amdgcn_sched_barrier(0);
-    uint8_t* slot = myring + cur * SG::SLOT;
-    TileRaw<KVF, D> t[HW];
-#pragma unroll
-    for (int hh = 0; hh < HW; ++hh) read_tile<KVF, D, HW>(slot, t[hh], col, grp, hh);
-    // the slot is refilled (NS tiles ahead) once every lane has read it
-    __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-    const int kn = k + NS * stride;
-    if (kn < ke) cp.issue(slot, kn, ke, lbs, nb_next, kbase, vbase, row_stride);
-    else wait_vmcnt_le<0>();                              // nothing more to issue: keep vmcnt exact
-    nb_next = WaveCopy<KVF, D, HW>::blocks(kn + stride, ke, lbs, table);
-    __builtin_amdgcn_sched_barrier(0);
+  // One piece: keys [k0, k1) of segment (b, hg), whose sequence starts at row
+  // q0 and holds past + 1 keys.  nparts == 1: the piece is the whole segment.
+  // Otherwise its partial goes to slot `slot`, and the last of the segment's
+  // nparts pieces to arrive merges the slots part_slot(0 .. nparts-1).
+  // spec: the block ids of this wave's first tile read early for the range
+  // [spec_kb, spec_ke) (used if the true range names the same entries), or
+  // {-1, -1}.
+  auto run_piece = [&](int b, int hg, int k0, int k1, int q0, int past,
+                       typename WC::Blocks spec, int spec_kb, int spec_ke, int nparts, int slot,
+                       auto part_slot) {
+    const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+    const uint8_t* kbase = a.key_cache + (size_t)hg * SG::RB;
+    const uint8_t* vbase = a.value_cache + (size_t)hg * SG::RB;
+    const int kb = k0 + 32 * wave, ke = k1;
+    const bool spec_ok = spec.b0 >= 0 &&
+                         WC::entry(kb, ke, lbs, 0) == WC::entry(spec_kb, spec_ke, lbs, 0) &&
+                         WC::entry(kb, ke, lbs, 1) == WC::entry(spec_kb, spec_ke, lbs, 1);
+    // query and key-scale loads go out first, then this wave's first NS tiles
+    QueryRaw<D, SM> qraw[HW];
 #pragma unroll
     for (int hh = 0; hh < HW; ++hh)
-      compute_tile<KVF, D>(t[hh], k, ke, c2[hh], qhi[hh], qlo[hh], st[hh], grp);
-    cur = (cur + 1 == NS) ? 0 : cur + 1;
-  }
-  wait_vmcnt_le<0>();
-  __builtin_amdgcn_sched_barrier(0);
+      load_query<D, SM, TQ>(a, hg * HW + hh, q0, G, col, grp, qraw[hh]);
+    if (kb < ke)
+      cp.issue(myring, kb, ke, lbs, spec_ok ? spec : WC::blocks(kb, ke, lbs, table), kbase,
+               vbase, row_stride);
+#pragma unroll
+    for (int j = 1; j < NS; ++j)
+      if (kb + j * stride < ke)
+        cp.issue(myring + j * SG::SLOT, kb + j * stride, ke, lbs, table, kbase, vbase, row_stride);
+    // The waits below count NS - 1 tiles in flight behind the current one;
+    // with fewer tiles than that, wait for everything instead.
+    if (kb + (NS - 1) * stride >= ke) wait_vmcnt_le<0>();
 
-  // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
-  __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];        // running max, sum per wave
-  float* wo = reinterpret_cast<float*>(myring);            // [HW][kDecMaxGroup][D] per wave
-  static_assert(HW * kDecMaxGroup * D * 4 <= NS * SG::SLOT, "merge area");
+    f16x8 qhi[HW][NQK], qlo[HW][NQK];
+    float c2[HW];
 #pragma unroll
-  for (int hh = 0; hh < HW; ++hh) {
-    const float l_run = rows_sum(st[hh].l);
-    if (col < G) {
-      if (grp == 0) { sm_ml[wave][hh][0][col] = st[hh].m; sm_ml[wave][hh][1][col] = l_run; }
-#pragma unroll
-      for (int nbk = 0; nbk < NPV; ++nbk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          wo[(hh * kDecMaxGroup + col) * D + (D / 16) * (4 * grp + r) + nbk] = st[hh].o[nbk][r];
+    for (int hh = 0; hh < HW; ++hh) {
+      const int e = fold_loaded_query<D, KVF, SM, TQ>(qraw[hh], qhi[hh], qlo[hh]);
+      c2[hh] = score_factor_log2(a.softmax_scale, e, kKeyOperandScale<KVF>);   // raw -> log2 units
     }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < HW * G * D; t += NW * 64) {
-    const int hh = t / (G * D), cq = (t / D) % G, d = t % D;
-    float M = -INFINITY;
+
+    WaveState<D> st[HW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][hh][0][cq]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
+    for (int hh = 0; hh < HW; ++hh)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2(sm_ml[w][hh][0][cq] - M);
-        L += f * sm_ml[w][hh][1][cq];
-        O += f * reinterpret_cast<const float*>(ring[w])[(hh * kDecMaxGroup + cq) * D + d];
+      for (int i = 0; i < NPV; ++i) st[hh].o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    int cur = 0;
+    // block ids of the next tile to issue, fetched one iteration ahead
+    typename WC::Blocks nb_next = WC::blocks(kb + NS * stride, ke, lbs, table);
+    for (int k = kb; k < ke; k += stride) {
+      // this tile's copies are done once at most the later tiles' remain
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_le<(NS - 1) * 2 * SG::NI>();
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* slotp = myring + cur * SG::SLOT;
+      TileRaw<KVF, D> t[HW];
+#pragma unroll
+      for (int hh = 0; hh < HW; ++hh) read_tile<KVF, D, HW>(slotp, t[hh], col, grp, hh);
+      // the slot is refilled (NS tiles ahead) once every lane has read it
+      __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      const int kn = k + NS * stride;
+      if (kn < ke) cp.issue(slotp, kn, ke, lbs, nb_next, kbase, vbase, row_stride);
+      else wait_vmcnt_le<0>();                            // nothing more to issue: keep vmcnt exact
+      nb_next = WC::blocks(kn + stride, ke, lbs, table);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hh = 0; hh < HW; ++hh)
+        compute_tile<KVF, D>(t[hh], k, ke, c2[hh], qhi[hh], qlo[hh], st[hh], grp);
+      cur = (cur + 1 == NS) ? 0 : cur + 1;
+    }
+    wait_vmcnt_le<0>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- merge the waves of each head through LDS (each wave writes its own ring) ----
+    float* wo = reinterpret_cast<float*>(myring);          // [HW][kDecMaxGroup][D] per wave
+    static_assert(HW * kDecMaxGroup * D * 4 <= NS * SG::SLOT, "merge area");
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const float l_run = rows_sum(st[hh].l);
+      if (col < G) {
+        if (grp == 0) { sm_ml[wave][hh][0][col] = st[hh].m; sm_ml[wave][hh][1][col] = l_run; }
+#pragma unroll
+        for (int nbk = 0; nbk < NPV; ++nbk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            wo[(hh * kDecMaxGroup + col) * D + (D / 16) * (4 * grp + r) + nbk] = st[hh].o[nbk][r];
+      }
+      if (wave == 0 && lane == 0) sm_c2[hh] = c2[hh];
+    }
+    __syncthreads();
+    const bool direct = nparts == 1;
+    for (int t = threadIdx.x; t < HW * G * D; t += NW * 64) {
+      const int hh = t / (G * D), cq = (t / D) % G, d = t % D;
+      const float cf = sm_c2[hh];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[w][hh][0][cq]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = fast_exp2((sm_ml[w][hh][0][cq] - M) * cf);
+          L += f * sm_ml[w][hh][1][cq];
+          O += f * reinterpret_cast<const float*>(ring[w])[(hh * kDecMaxGroup + cq) * D + d];
+        }
+      }
+      const int ho = hg * HW + hh;
+      const int hq = ho * G + cq;
+      if (direct) {
+        const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
+        const float val = (L > 0.f) ? v_unbias<KVF>(O / L, d) * vs : 0.f;   // both carry 2^7
+        reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
+      } else {
+        // this piece's partial: normalised output (value scale not applied),
+        // its raw maximum and its sum (which carries 2^7, like every piece's)
+        const size_t pi = (size_t)slot * HW * G + hh * G + cq;
+        store_agent(&a.part_o[pi * D + d], (L > 0.f) ? v_unbias<KVF>(O / L, d) : 0.f);
+        if (d == 0) {
+          store_agent(&a.part_ml[2 * pi], M);
+          store_agent(&a.part_ml[2 * pi + 1], L);
+        }
       }
     }
-    const int ho = blockIdx.x * HW + hh;
-    const int hq = ho * G + cq;
-    if constexpr (SPLIT) {
-      // partial of this workgroup's chunks (value scale not applied) and its
-      // log-sum-exp (both O and L carry 2^7)
-      const size_t pi = ((size_t)q0 * H + hq) * a.part_count + blockIdx.z;
-      a.part_o[pi * D + d] = (L > 0.f) ? v_unbias<KVF>(O / L, d) : 0.f;
-      if (d == 0) a.part_lse[pi] = (L > 0.f) ? (M + __log2f(L) - kPScaleLog2) * kLn2 : -INFINITY;
-    } else {
-      const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + d] : a.v_scale[ho];
-      const float val = (L > 0.f) ? v_unbias<KVF>(O / L, d) * vs : 0.f;   // both carry 2^7
-      reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + d] = from_f32<TQ>(val);
+    if (direct) {
+      __syncthreads();                                     // the rings are reused next
+      return;
+    }
+
+    // ---- arrival: the last piece of this segment merges ----
+    // Every thread's partial stores are device-coherent and complete before
+    // the barrier, so they precede the counter increment; the last piece to
+    // arrive reads the others' partials with device-coherent loads.
+    wait_stores();
+    __syncthreads();
+    int32_t* ctr = a.dec_counters + (size_t)b * hgs + hg;
+    if (threadIdx.x == 0)
+      sm_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                nparts - 1;
+    __syncthreads();
+    if (!sm_last) return;
+    // Merge: every thread takes two output elements and runs a merge over
+    // the pieces by their raw maxima, 16 pieces at a time with all their loads
+    // (maximum, sum and the two outputs) issued together, so the merge costs
+    // one memory round trip per 16 pieces.
+    constexpr int NT = NW * 64, U = 16;
+    for (int t0 = threadIdx.x; t0 < HW * G * D; t0 += 2 * NT) {
+      int pr[2], dd[2];
+      bool on[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int t = t0 + e * NT;
+        on[e] = t < HW * G * D;
+        pr[e] = on[e] ? t / D : 0;
+        dd[e] = on[e] ? t % D : 0;
+      }
+      float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f}, O[2] = {0.f, 0.f};
+      for (int p0 = 0; p0 < nparts; p0 += U) {
+        float pm[2][U], pl[2][U], po[2][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = p0 + u < nparts;
+          const size_t sl = ok ? (size_t)part_slot(p0 + u) * HW * G : 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const size_t pi = sl + pr[e];
+            pm[e][u] = (ok && on[e]) ? load_agent(&a.part_ml[2 * pi]) : -INFINITY;
+            pl[e][u] = (ok && on[e]) ? load_agent(&a.part_ml[2 * pi + 1]) : 0.f;
+            po[e][u] = (ok && on[e]) ? load_agent(&a.part_o[pi * D + dd[e]]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float cf = sm_c2[pr[e] / G];
+          float mn = M[e];
+#pragma unroll
+          for (int u = 0; u < U; ++u) mn = fmaxf(mn, pm[e][u]);
+          if (mn == -INFINITY) continue;                   // only empty pieces so far
+          const float sc = fast_exp2((M[e] - mn) * cf);    // 0 while M is -inf
+          L[e] *= sc;
+          O[e] *= sc;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const float wgt = fast_exp2((pm[e][u] - mn) * cf) * pl[e][u];   // empty: 0
+            L[e] += wgt;
+            O[e] = fmaf(wgt, po[e][u], O[e]);
+          }
+          M[e] = mn;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (!on[e]) continue;
+        const int ho = hg * HW + pr[e] / G;
+        const int hq = ho * G + pr[e] % G;
+        const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[ho * D + dd[e]] : a.v_scale[ho];
+        reinterpret_cast<TQ*>(a.out)[((size_t)q0 * H + hq) * D + dd[e]] =
+            from_f32<TQ>((L[e] > 0.f) ? O[e] / L[e] * vs : 0.f);
+      }
+    }
+    // every counter is zero again when the launch ends
+    if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();                                       // the rings are reused next
+  };
+
+  if constexpr (MODE == DEC_SINGLE || MODE == DEC_CHUNKS) {
+    const int hg = (int)(blockIdx.x % (unsigned)hgs);     // consecutive workgroups: other XCDs
+    const int item = (int)(blockIdx.x / (unsigned)hgs);
+    const int P = MODE == DEC_SINGLE ? 1 : a.dec_parts_per_seq;
+    const int b = item / P, j = item % P;
+    const int32_t* __restrict__ table = block_table + (size_t)b * a.max_blocks;
+    // The first tile's block ids are read before this sequence's length
+    // arrives, for the batch's longest length (inside the table row either
+    // way); they serve whenever the true range names the same table entries,
+    // which saves the table round trip before the first copy.
+    int k0s = 0, k1s = a.max_kv_len;
+    if constexpr (MODE == DEC_CHUNKS) chunk_part_keys(a, j, a.max_kv_len, k0s, k1s);
+    const typename WC::Blocks spec = WC::blocks(k0s + 32 * wave, k1s, lbs, table);
+    const int q0 = a.cum_q[b];
+    const int past = a.past_lens[b];
+    // no new token: no rows.  The test also reads the past and the speculative
+    // entries (a negative past never occurs), so all these loads go out
+    // together instead of one behind the other.
+    if ((a.cum_q[b + 1] == q0) | ((past < 0) & (spec.b0 == spec.b1))) return;
+    const int kv_len = past + 1;
+    int k0 = 0, k1 = kv_len;
+    if constexpr (MODE == DEC_CHUNKS) chunk_part_keys(a, j, kv_len, k0, k1);
+    run_piece(b, hg, k0, k1, q0, past, spec, k0s + 32 * wave, k1s, P, (int)blockIdx.x,
+              [&](int p) { return (b * P + p) * hgs + hg; });
+  } else {
+    // Stream partition: this workgroup's run of the concatenated tiles.
+    const long long T = a.dec_total_tiles;
+    const int N = (int)gridDim.x;
+    const int w = (int)blockIdx.x;
+    long long g = (long long)w * T / N;
+    const long long g1 = (long long)(w + 1) * T / N;
+    if (g >= g1) return;
+    StreamPos pos = stream_find(a.cum_q, a.past_lens, a.batch, hgs, g);
+    int b = __builtin_amdgcn_readfirstlane(pos.b);
+    if (b < 0) return;
+    int tiles = __builtin_amdgcn_readfirstlane(pos.tiles);
+    int off = __builtin_amdgcn_readfirstlane(pos.off);
+    int q0 = __builtin_amdgcn_readfirstlane(pos.q0);
+    int past = __builtin_amdgcn_readfirstlane(pos.past);
+    long long seq_first = g - off;                         // first global tile of sequence b
+    int hg = off / tiles, t = off % tiles;
+    bool first = true;
+    for (;;) {
+      const int n = (int)min((long long)(tiles - t), g1 - g);
+      const long long seg = seq_first + (long long)hg * tiles;   // the segment's first tile
+      const int kv_len = past + 1;
+      int nparts = 1, slot = 0, wfirst = 0;
+      if (!(t == 0 && n == tiles)) {
+        wfirst = stream_owner(seg, T, N);
+        nparts = stream_owner(seg + tiles - 1, T, N) - wfirst + 1;
+        slot = 2 * w + (first ? 0 : 1);
+      }
+      run_piece(b, hg, 32 * t, min(kv_len, 32 * (t + n)), q0, past,
+                typename WC::Blocks{-1, -1}, 0, 0, nparts, slot, [&](int p) {
+                  // a piece is its workgroup's first unless that workgroup
+                  // started before the segment (then it is its last)
+                  const int wp = wfirst + p;
+                  return 2 * wp + ((long long)wp * T / N < seg ? 1 : 0);
+                });
+      g += n;
+      if (g >= g1) break;
+      first = false;
+      t = 0;
+      if (++hg == hgs) {
+        // next sequence with a new row
+        hg = 0;
+        seq_first += (long long)hgs * tiles;
+        do {
+          ++b;
+          if (b >= a.batch) return;
+          q0 = a.cum_q[b];
+          past = a.past_lens[b];
+          tiles = a.cum_q[b + 1] > q0 ? (past + 32) >> 5 : 0;
+        } while (tiles == 0);
+      }
     }
   }
 }
@@ -688,33 +888,36 @@ bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype)
          block_size >= 16 && block_size % 16 == 0 && (q_dtype == DT_F16 || q_dtype == DT_BF16);
 }
 
-// Launch with HW heads per wave.  Single pass: grid (hkv / HW, batch), 8 waves
-// per (sequence, head group), NS = 1 tile in flight per wave besides the one
-// being read (the copies of 8 waves then keep ~64 KB per CU in flight, where
-// measured HBM efficiency peaks).  Split-KV: grid (hkv / HW, batch,
-// ceil(S / NW)), one wave per chunk, NS = 1 as well (a second tile in flight
-// per wave measured 4 % slower on 128 chunks of 32k keys); NW = 8 waves per workgroup when
-// that still gives every compute unit a workgroup, else 4.
+// Launch: a 1-D grid of (parts x head groups) workgroups of NW waves, NS = 1
+// tile in flight per wave besides the one being read (the copies of 8 waves
+// then keep ~64 KB per CU in flight, where measured HBM efficiency peaks).
+// The partition, the part count and the waves per workgroup come from the
+// host plan.
 template <int D, int KVF, int SM, typename TQ, int HW, int NW>
-static void launch_split_nw(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.hkv / HW, a.batch, (a.num_splits + NW - 1) / NW);
-  hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, NW, 1, HW, true>), grid,
-                     dim3(NW * 64), 0, st, a, a.block_table);
+static int launch_nw(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.grid_x), block(NW * 64);
+  switch (a.dec_mode) {
+    case DEC_SINGLE:
+      hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, NW, 1, HW, DEC_SINGLE>), grid,
+                         block, 0, st, a, a.block_table);
+      return 0;
+    case DEC_CHUNKS:
+      hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, NW, 1, HW, DEC_CHUNKS>), grid,
+                         block, 0, st, a, a.block_table);
+      return 0;
+    case DEC_STREAM:
+      hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, NW, 1, HW, DEC_STREAM>), grid,
+                         block, 0, st, a, a.block_table);
+      return 0;
+  }
+  return -1;
 }
 
 template <int D, int KVF, int SM, typename TQ, int HW>
 static int launch_hw_q(const AttnArgs& a, hipStream_t st) {
-  if (a.num_splits > 1) {
-    if (decode_split_waves(a.hkv, HW, a.batch, a.num_splits, a.num_cus) == 8)
-      launch_split_nw<D, KVF, SM, TQ, HW, 8>(a, st);
-    else
-      launch_split_nw<D, KVF, SM, TQ, HW, 4>(a, st);
-  } else {
-    dim3 grid(a.hkv / HW, a.batch, 1);
-    hipLaunchKernelGGL((decode_stream_kernel<D, KVF, SM, TQ, 8, 1, HW, false>), grid,
-                       dim3(8 * 64), 0, st, a, a.block_table);
-  }
-  return 0;
+  if (a.dec_waves == 8) return launch_nw<D, KVF, SM, TQ, HW, 8>(a, st);
+  if (a.dec_waves == 4) return launch_nw<D, KVF, SM, TQ, HW, 4>(a, st);
+  return -1;
 }
 
 template <int D, int KVF, int SM, int HW>
@@ -730,7 +933,9 @@ template <int D, int KVF, int SM>
 static int launch_dq(const AttnArgs& a, hipStream_t st) {
   constexpr int C = KvGeom<KVF, D>::C;
   static_assert(C == 32 || C == 64 || C == 128, "row bytes");
-  switch (decode_heads_per_wave(KVF, D, a.hkv)) {
+  const int hw = decode_heads_per_wave(KVF, D, a.hkv);
+  if (a.hkv / hw != a.dec_head_groups) return -1;
+  switch (hw) {
     case 1: return launch_hw<D, KVF, SM, 1>(a, st);
     case 2: if constexpr (C <= 64) return launch_hw<D, KVF, SM, 2>(a, st); break;
     case 4: if constexpr (C <= 32) return launch_hw<D, KVF, SM, 4>(a, st); break;
@@ -753,6 +958,7 @@ static int launch_d(const AttnArgs& a, hipStream_t st) {
 
 int launch_decode_mfma(const AttnArgs& a, hipStream_t st) {
   if (!decode_mfma_supports(a.head_size, a.num_heads / a.hkv, a.block_size, a.q_dtype)) return -1;
+  if (a.dec_mode != DEC_SINGLE && (!a.part_o || !a.part_ml || !a.dec_counters)) return -1;
   return a.head_size == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
 }
 

@@ -175,18 +175,87 @@ __device__ __forceinline__ float rows_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Softmax numerators 2^(s*c - m + e) in an fp16 P, with m the running maximum
-// (in log2 units, a rounded product s*c) and e the scale exponent of P.
-// Below |m| = kHugeScoreLog2 they are computed as exp2(fma(s, c, e - m)): the
-// exact product against m and the rounding of e - m each stay within 1/8, so
-// with the lazy-maximum slack the argument stays under 15.5 and P under 2^16.
-// Past it (key scales far beyond the 16-bit ranges, a hard-argmax softmax) the
-// product is rounded first, as the maximum was, and the difference to m is
-// taken before adding e: exact near the maximum at every magnitude.
+// ---------------------------------------------------------------------------
+// Device-coherent stores and loads (agent-scope relaxed atomics: global_store /
+// global_load with sc1, coherent across the XCDs' L2 caches) for the values
+// one workgroup hands to another inside a launch.  Ordering comes from the
+// writer waiting for its stores (s_waitcnt vmcnt(0)) before it signals, not
+// from a fence: an agent-scope fence would write back and invalidate the whole
+// L2 of the XCD.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0), other counters untouched
+}
+
+// ---------------------------------------------------------------------------
+// Key-scale normaliser ("ONNX Runtime: INT4 Paged KV Cache", section 3: the
+// per-channel key scale is folded into the query after dividing by a power of
+// two of the kv head's largest scale, so the 16-bit operand cannot overflow).
+// M = 2^e with e = ceil(log2 max|s|), capped at 127 (the largest fp32 power of
+// two), so every finite scale -- FLT_MAX and subnormals included -- gives a
+// finite M and s / M = ldexp(s, -e) exact with |s / M| < 2.  max|s| = 0 gives
+// e = 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int scale_exponent(float smax) {
+  if (!(smax > 0.f)) return 0;
+  int ex;
+  const float fr = frexpf(smax, &ex);                      // smax = fr * 2^ex, fr in [0.5, 1)
+  return min(fr == 0.5f ? ex - 1 : ex, 127);
+}
+
+// scale_exponent of kv head g's key scales, computed by a whole workgroup
+// (blockDim.x a multiple of 64, >= D; *slot is LDS scratch).  Every thread
+// returns the same value.
+template <int SM>
+__device__ __forceinline__ int key_scale_exponent(const float* k_scale, int g, int D, int* slot) {
+  float m;
+  if constexpr (SM == SCALE_CHANNEL) {
+    m = (int)threadIdx.x < D ? fabsf(k_scale[g * D + threadIdx.x]) : 0.f;
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (threadIdx.x == 0) *slot = 0;
+    __syncthreads();
+    // non-negative floats order like their bit patterns
+    if ((threadIdx.x & 63) == 0) atomicMax(slot, __float_as_int(m));
+    __syncthreads();
+    m = __int_as_float(*slot);
+  } else {
+    m = fabsf(k_scale[g]);
+  }
+  return scale_exponent(m);
+}
+
+// The factor that turns a raw score (query' . key operand) into log2 units:
+// softmax_scale * 2^e * log2(e) / key_operand_scale, clamped into
+// [FLT_MIN, FLT_MAX].  Past FLT_MAX every score gap the raw scores can
+// resolve is already a hard argmax; below FLT_MIN every logit is below
+// 2^-100 and the softmax is uniform to fp32 precision.  Keeping the factor
+// finite and positive is what lets the kernels form every exponent as
+// (raw - raw_max) * factor without an infinity or a NaN.
+__device__ __forceinline__ float score_factor_log2(float softmax_scale, int e, float key_op_scale) {
+  const float r = ldexpf(softmax_scale * 1.4426950408889634f / key_op_scale, e);
+  return fminf(fmaxf(r, 0x1p-126f), 0x1.fffffep127f);
+}
+
+// Softmax numerators 2^(c * (s - m) + e) in an fp16 P: s a raw score, m the
+// running maximum of the raw scores, c the score factor (log2 units, finite,
+// see score_factor_log2) and e the scale exponent of P.  While |c * m| stays
+// below kHugeScoreLog2 they are computed as exp2(fma(s, c, e - c * m)): the
+// exact product against the rounded c * m and the rounding of e - c * m each
+// stay within 1/8, so with the lazy-maximum slack the argument stays under
+// 15.5 and P under 2^16.  Past it (key scales far beyond the 16-bit ranges: a
+// hard-argmax softmax) the difference s - m is taken first -- exact near the
+// maximum (Sterbenz) -- and only then scaled, so no product of a huge factor
+// and a huge score is ever formed and nothing overflows.
 constexpr float kHugeScoreLog2 = 0x1p22f;
-__device__ __forceinline__ float huge_score_arg(float s, float c, float m, float e) {
+__device__ __forceinline__ float safe_score_arg(float s, float m, float c, float e) {
 #pragma clang fp contract(off)
-  return (s * c - m) + e;
+  return (s - m) * c + e;
 }
 
 }  // namespace paq

@@ -40,19 +40,29 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* cum_q;
   const int32_t* past_lens;
-  float* part_o;        // split-KV partial outputs [T][H][S][D] (fp32), or null
-  float* part_lse;      // split-KV partial log-sum-exps [T][H][S], or null
+  // fp32 kernel split-KV: partial outputs [T][H][S][D] and their log-sum-exps
+  // as (raw maximum, log2 sum) pairs [T][H][S][2]; MFMA decode parts: partial
+  // outputs [parts][H][D] and (raw maximum, sum) pairs [parts][H][2]
+  float* part_o;
+  float* part_lse;
+  float* part_ml;
+  int32_t* dec_counters; // MFMA decode: arrival counter per (sequence, head group), zero
   int batch, token_count, num_heads, hkv, head_size, block_size, max_blocks;
   int q_dtype, kv_format, scale_mode;
   int num_splits;       // 1 = single pass (no partials)
-  int part_count;       // split-KV: partials per (row, head) in the workspace
-  int grid_x;           // launch grid (1-D prefill: from the host plan)
+  int part_count;       // fp32 split-KV: partials per (row, head) in the workspace
+  int grid_x;           // 1-D launch grid (MFMA decode and prefill: from the host plan)
   int pf_ntq;           // prefill: query tiles of every sequence if all have the same, else 0
   int max_query_len;    // exact, from the host cum_q
   int max_kv_len;       // longest sequence with new rows (host)
   int block_size_log2;  // block_size is a power of two
-  int num_cus;          // compute units of the device (split-KV grid sizing)
-  int split_chunks_per_wg;  // split-KV: consecutive chunks per workgroup (set by the launcher)
+  // MFMA decode partition (host plan)
+  int dec_mode;            // DEC_SINGLE / DEC_CHUNKS / DEC_STREAM
+  int dec_waves;           // waves per workgroup (4 or 8)
+  int dec_head_groups;     // kv_num_heads / heads per wave
+  int dec_parts_per_seq;   // DEC_CHUNKS: parts of every sequence
+  int dec_chunks_per_part; // DEC_CHUNKS: consecutive chunks per part
+  long long dec_total_tiles;  // DEC_STREAM: 32-key tiles of all segments
   float softmax_scale;  // already resolved (> 0)
 };
 
@@ -66,12 +76,16 @@ inline int decode_heads_per_wave(int kv_format, int head_size, int hkv) {
   while (hw > 1 && hkv % hw) hw /= 2;
   return hw;
 }
-// Decode split-KV: waves (one per chunk) per workgroup -- 8 when the grid
-// still gives every compute unit a workgroup, else 4.
-inline int decode_split_waves(int hkv, int heads_per_wave, int batch, int splits, int num_cus) {
-  const long waves = (long)(hkv / heads_per_wave) * batch * splits;
-  return waves >= 8L * (num_cus > 0 ? num_cus : 256) ? 8 : 4;
-}
+// MFMA decode partitions (see decode_mfma.hip).
+enum { DEC_SINGLE = 0, DEC_CHUNKS = 1, DEC_STREAM = 2 };
+// Arrival counters at the head of every decode workspace: one int32 per
+// (sequence, head group) of a split call, zero before a call and after it.
+constexpr int kDecCounters = 16384;
+// Pieces one segment may be cut into (the last one to arrive merges them all
+// at once: their weights must fit its LDS); the stream partition uses at most
+// this many workgroups.
+constexpr int kDecMaxPartsPerSeq = 256;
+constexpr size_t kDecCounterBytes = (size_t)kDecCounters * 4;
 // Prefill (MFMA): workgroups of 4 waves x 32 / group tokens.  (Sequence, kv
 // head) pair p runs on XCD p % 8 and needs ceil(q_len / tokens) query tiles;
 // the 1-D grid is 8 x the largest per-XCD tile count, so no workgroup is
@@ -115,6 +129,8 @@ int launch_sparse_compact(const int32_t* block_table, int max_blocks, const int3
 
 // Shape support of the MFMA kernels (host checks before choosing a path).
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype);
+// The portable fp32 kernel serves GQA groups up to this size.
+constexpr int kF32KernelMaxGroup = 16;
 bool prefill_mfma_supports(int head_size, int group, int block_size, int q_dtype);
 
 }  // namespace paq

@@ -124,8 +124,21 @@ int device_cu_count(int* out) {
   return PAQ_OK;
 }
 
+// Compute units to plan for: the caller's count, else the current device's,
+// else (no device visible: sizing on a host without a GPU) 256.
+int resolve_cus(int num_cus) {
+  if (num_cus > 0) return num_cus;
+  int n = 0;
+  if (device_cu_count(&n) == PAQ_OK) return n;
+  return 256;
+}
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Length-balanced (stream) decode: about one workgroup per compute unit, each
+// streaming at least kStreamMinTiles 32-key tiles (two per wave).
+constexpr int kStreamMinTiles = 16;
 
 int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
                 int num_splits, int num_cus, paq_plan* p) {
@@ -133,13 +146,13 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
   SeqStats st;
   int rc = validate(d, cum_q_host, past_host, &st);
   if (rc) return rc;
-  if (num_splits < 0) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d < 0", num_splits);
   for (int b = 0; b < d->batch; ++b) {
     const int q = cum_q_host[b + 1] - cum_q_host[b];
     if (q > 1)
       return fail(PAQ_ERR_INVALID_ARG,
                   "decode needs q_len in {0,1}; sequence %d has %d new tokens", b, q);
   }
+  if (num_splits > 4096) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d > 4096", num_splits);
   p->max_query_len = st.max_q;
   p->max_kv_len = st.max_kv;
   p->active_seqs = st.active;
@@ -152,49 +165,139 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
   const bool mfma = d->q_dtype != PAQ_DT_F32 &&
                     paq::decode_mfma_supports(d->head_size, group, d->block_size, d->q_dtype);
   const int max_nb = (st.max_kv + d->block_size - 1) / d->block_size;
-  int S = num_splits;
-  if (S == 0) {
+  const int cus = resolve_cus(num_cus);
+  const size_t head = paq::kDecCounterBytes;
+  if (!mfma) {
+    if (group > paq::kF32KernelMaxGroup)
+      return fail(PAQ_ERR_UNSUPPORTED,
+                  "no decode kernel for %s queries with %d query heads per kv head "
+                  "(the fp32 kernel takes at most %d)",
+                  d->q_dtype == PAQ_DT_F32 ? "fp32" : "16-bit", group, paq::kF32KernelMaxGroup);
     // Flash-decoding rule ("GQA GEMV decode", section 2): split the KV of a
     // sequence only when the (sequence, kv head) units under-fill the device
     // and a sequence has more than one KV chunk.  Aim at two workgroups per CU
-    // with chunks of at least 256 keys.
-    S = 1;
-    if (num_cus <= 0) {
-      rc = device_cu_count(&num_cus);
-      if (rc) return rc;
+    // with chunks of at least 256 keys.  (A length-balanced request takes the
+    // same rule.)
+    int S = num_splits;
+    if (S <= 0) {
+      S = 1;
+      if (p->work_units < cus && max_nb > 1) {
+        const int want = (2 * cus + p->work_units - 1) / p->work_units;
+        const int by_len = std::max(1, st.max_kv / 256);
+        S = std::max(1, std::min(std::min(want, by_len), max_nb));
+      }
     }
-    if (p->work_units < num_cus && max_nb > 1) {
-      const int want = (2 * num_cus + p->work_units - 1) / p->work_units;
-      const int by_len = std::max(1, st.max_kv / 256);
-      S = std::max(1, std::min(std::min(want, by_len), max_nb));
-    }
-  }
-  if (S > 4096) return fail(PAQ_ERR_INVALID_ARG, "num_splits %d > 4096", S);
-  // chunk bounds are computed as chunk * blocks / num_splits in 32-bit unsigned
-  if (S > 1 && (unsigned long long)(S + 1) * (unsigned long long)d->max_blocks_per_seq >=
-                   (1ull << 32))
-    return fail(PAQ_ERR_UNSUPPORTED, "num_splits %d x max_blocks_per_seq %d too large", S,
-                d->max_blocks_per_seq);
-  p->num_splits = S;
-  if (mfma) {
-    p->path = S > 1 ? PAQ_PATH_SPLIT : PAQ_PATH_SINGLE;
-    const int hw = paq::decode_heads_per_wave(d->kv_format, d->head_size, d->kv_num_heads);
-    p->grid_x = d->kv_num_heads / hw;
-    p->grid_y = d->batch;
-    p->grid_z = S > 1 ? (S + paq::decode_split_waves(d->kv_num_heads, hw, d->batch, S, num_cus) -
-                         1) / paq::decode_split_waves(d->kv_num_heads, hw, d->batch, S, num_cus)
-                      : 1;
-  } else {
+    if (S > 1 && (unsigned long long)(S + 1) * (unsigned long long)d->max_blocks_per_seq >=
+                     (1ull << 32))
+      return fail(PAQ_ERR_UNSUPPORTED, "num_splits %d x max_blocks_per_seq %d too large", S,
+                  d->max_blocks_per_seq);
+    p->num_splits = S;
     p->path = S > 1 ? PAQ_PATH_F32_SPLIT : PAQ_PATH_F32_SINGLE;
     p->grid_x = d->token_count;
     p->grid_y = d->kv_num_heads;
     p->grid_z = S;
+    p->waves_per_group = 4;
+    if (S > 1) {
+      const size_t rows = (size_t)d->token_count * d->num_heads * S;
+      p->workspace_bytes = head + align_up(rows * d->head_size * sizeof(float)) +
+                           align_up(rows * 2 * sizeof(float));
+    }
+    return PAQ_OK;
   }
-  if (S > 1) {
-    // one partial per (row, head) and grid slice: a workgroup of the MFMA
-    // kernel merges its chunks first, the fp32 kernel writes one per chunk
-    const size_t rows = (size_t)d->token_count * d->num_heads * p->grid_z;
-    p->workspace_bytes = align_up(rows * d->head_size * sizeof(float)) + align_up(rows * sizeof(float));
+
+  // MFMA decode: workgroups of 8 waves over one head group (HW adjacent kv
+  // heads) and one part of one sequence.
+  const int hw = paq::decode_heads_per_wave(d->kv_format, d->head_size, d->kv_num_heads);
+  const int hg = d->kv_num_heads / hw;
+  const long units = (long)st.active * hg;
+  const bool counters_fit = (long)d->batch * hg <= paq::kDecCounters;
+  int mode = paq::DEC_SINGLE, S = 1;
+  long groups = 0;                    // stream partition: workgroups
+  long total = 0;                     // stream partition: tiles of all segments
+  for (int b = 0; b < d->batch; ++b)
+    if (cum_q_host[b + 1] > cum_q_host[b]) total += ((long)past_host[b] + 32) / 32;
+  total *= hg;
+  if (num_splits > 1) {
+    if (!counters_fit)
+      return fail(PAQ_ERR_UNSUPPORTED, "split decode of %d sequences x %d head groups: at most %d",
+                  d->batch, hg, paq::kDecCounters);
+    if ((unsigned long long)(num_splits + 1) * (unsigned long long)d->max_blocks_per_seq >=
+        (1ull << 32))
+      return fail(PAQ_ERR_UNSUPPORTED, "num_splits %d x max_blocks_per_seq %d too large",
+                  num_splits, d->max_blocks_per_seq);
+    mode = paq::DEC_CHUNKS;
+    S = num_splits;
+  } else if (num_splits < 0) {
+    if (!counters_fit)
+      return fail(PAQ_ERR_UNSUPPORTED, "split decode of %d sequences x %d head groups: at most %d",
+                  d->batch, hg, paq::kDecCounters);
+    groups = -(long)num_splits;
+    if (groups > paq::kDecMaxPartsPerSeq)
+      return fail(PAQ_ERR_UNSUPPORTED, "a length-balanced decode over %ld workgroups: at most %d",
+                  groups, paq::kDecMaxPartsPerSeq);
+    mode = paq::DEC_STREAM;
+  } else if (num_splits == 0 && counters_fit && units < cus && max_nb > 1) {
+    // Automatic: the flash-decoding rule of "GQA GEMV decode" (section 2):
+    // split the KV of the sequences only when the (sequence, kv head) units
+    // under-fill the device.  With near-uniform lengths, block-aligned chunks
+    // of every sequence (about two workgroups per compute unit, chunks of at
+    // least 256 keys); with skewed lengths the length-balanced partition,
+    // which deals every compute unit the same share of all tiles.
+    long sum_kv = 0;
+    for (int b = 0; b < d->batch; ++b)
+      if (cum_q_host[b + 1] > cum_q_host[b]) sum_kv += (long)past_host[b] + 1;
+    // (max > 1.5 x mean, and long enough for a split to pay: 512 keys)
+    const bool skewed = 2L * st.max_kv * st.active > 3L * sum_kv && st.max_kv >= 512;
+    if (skewed) {
+      groups = std::min<long>(std::min<long>(cus, paq::kDecMaxPartsPerSeq),
+                              std::max<long>(1, total / kStreamMinTiles));
+      mode = paq::DEC_STREAM;
+    } else {
+      const long want = (2L * cus + units - 1) / units;
+      const long by_len = std::max(1, st.max_kv / 256);
+      S = (int)std::max<long>(1, std::min<long>(std::min<long>(want, by_len), max_nb));
+      if (S > 1) mode = paq::DEC_CHUNKS;
+    }
+  }
+  p->path = mode == paq::DEC_SINGLE ? PAQ_PATH_SINGLE
+            : mode == paq::DEC_CHUNKS ? PAQ_PATH_SPLIT : PAQ_PATH_BALANCED;
+  p->waves_per_group = 8;
+  long parts, slots;
+  if (mode == paq::DEC_SINGLE) {
+    parts = d->batch;
+    slots = 0;
+    p->num_splits = 1;
+  } else if (mode == paq::DEC_CHUNKS) {
+    // about one workgroup per compute unit: parts of ceil(S / P) chunks each
+    long P = std::max<long>(1, std::min<long>(std::min<long>(S, paq::kDecMaxPartsPerSeq),
+                                              (cus + units - 1) / units));
+    const long cpw = (S + P - 1) / P;
+    P = (S + cpw - 1) / cpw;
+    p->num_splits = S;
+    p->parts_per_seq = (int)P;
+    p->chunks_per_part = (int)cpw;
+    parts = (long)d->batch * P;
+    slots = parts * hg;                 // one partial per workgroup
+  } else {
+    groups = std::min<long>(groups, std::max<long>(1, total));
+    p->num_splits = 0;
+    p->keys_per_group = (int)std::min<long>(32 * ((total + groups - 1) / groups), 1L << 30);
+    p->total_tiles = total;
+    parts = groups;
+    slots = 2 * groups;                 // a first and a last piece per workgroup
+  }
+  const long grid = mode == paq::DEC_STREAM ? parts : parts * hg;
+  if (grid > 0x7fffffffL) return fail(PAQ_ERR_UNSUPPORTED, "decode grid too large");
+  p->parts = (int)parts;
+  p->grid_x = (int)grid;
+  p->grid_y = 1;
+  p->grid_z = 1;
+  if (mode != paq::DEC_SINGLE) {
+    // per partial slot: (raw maximum, sum) and the output of the HW * G query
+    // heads of one head group
+    const size_t rows = (size_t)slots * (d->num_heads / hg);
+    p->workspace_bytes = head + align_up(rows * d->head_size * sizeof(float)) +
+                         align_up(rows * 2 * sizeof(float));
   }
   return PAQ_OK;
 }
@@ -222,6 +325,10 @@ int plan_prefill(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pa
     p->grid_y = 1;
     p->grid_z = 1;
   } else {
+    if (group > paq::kF32KernelMaxGroup)
+      return fail(PAQ_ERR_UNSUPPORTED,
+                  "no prefill kernel for %s queries with %d query heads per kv head",
+                  d->q_dtype == PAQ_DT_F32 ? "fp32" : "16-bit", group);
     p->path = PAQ_PATH_F32_PREFILL;
     p->grid_x = d->token_count;
     p->grid_y = d->kv_num_heads;
@@ -281,22 +388,41 @@ int launched(int launcher_rc, const char* what) {
 }
 
 // Decode launch shared by the dense and the block-sparse entry points: the
-// single-pass or split kernel, and the combine after a split.
+// kernels and launch shape the plan describes (the launchers recompute
+// nothing), and the fp32 kernel's combine after a split.  Workspace layout:
+// the arrival counters (kDecCounterBytes, zero before and after every call),
+// then the partials.
 int run_decode(const paq_desc* d, const paq_plan& p, paq::AttnArgs& a, void* workspace,
                hipStream_t st) {
   int rc;
-  if (p.num_splits > 1) {
-    rc = device_cu_count(&a.num_cus);
-    if (rc) return rc;
-    a.part_count = p.grid_z;
-    const size_t rows = (size_t)d->token_count * d->num_heads * a.part_count;
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + align_up(rows * d->head_size * sizeof(float)));
+  char* ws = (char*)workspace;
+  const size_t head = paq::kDecCounterBytes;
+  if (p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT || p.path == PAQ_PATH_BALANCED) {
+    a.dec_mode = p.path == PAQ_PATH_SINGLE ? paq::DEC_SINGLE
+                 : p.path == PAQ_PATH_SPLIT ? paq::DEC_CHUNKS : paq::DEC_STREAM;
+    a.dec_waves = p.waves_per_group;
+    a.dec_head_groups =
+        d->kv_num_heads / paq::decode_heads_per_wave(d->kv_format, d->head_size, d->kv_num_heads);
+    a.dec_parts_per_seq = p.parts_per_seq;
+    a.dec_chunks_per_part = p.chunks_per_part;
+    a.dec_total_tiles = p.total_tiles;
+    if (a.dec_mode != paq::DEC_SINGLE) {
+      const size_t slots = a.dec_mode == paq::DEC_STREAM ? 2 * (size_t)p.parts
+                                                          : (size_t)p.parts * a.dec_head_groups;
+      const size_t rows = slots * (d->num_heads / a.dec_head_groups);
+      a.dec_counters = (int32_t*)ws;
+      a.part_o = (float*)(ws + head);
+      a.part_ml = (float*)(ws + head + align_up(rows * d->head_size * sizeof(float)));
+    }
+    return launched(paq::launch_decode_mfma(a, st), "decode (MFMA)");
   }
-  if (p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT)
-    rc = launched(paq::launch_decode_mfma(a, st), "decode (MFMA)");
-  else
-    rc = launched(paq::launch_decode_f32(a, st), "decode (fp32)");
+  if (p.num_splits > 1) {
+    a.part_count = p.num_splits;
+    const size_t rows = (size_t)d->token_count * d->num_heads * a.part_count;
+    a.part_o = (float*)(ws + head);
+    a.part_lse = (float*)(ws + head + align_up(rows * d->head_size * sizeof(float)));
+  }
+  rc = launched(paq::launch_decode_f32(a, st), "decode (fp32)");
   if (rc) return rc;
   if (p.num_splits > 1) rc = launched(paq::launch_combine(a, st), "split-KV combine");
   return rc;
@@ -456,17 +582,26 @@ size_t paged_attn_decode_sparse_workspace_size(const paq_desc* d, const int32_t*
   return sparse_head_bytes(d->batch, max_sel) + p.workspace_bytes;
 }
 
-int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
-                           const void* key_cache, const void* value_cache,
-                           const float* k_scale, const float* v_scale,
-                           const int32_t* block_table, const int32_t* cum_q,
-                           const int32_t* past_lens, const int32_t* cum_q_host,
-                           const int32_t* past_lens_host, float softmax_scale,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Prefill launch.  padded_mql > 0 sizes the grid from that max_query_len
+// (every pair gets the same tile count; tiles past a sequence's rows exit at
+// once) instead of the exact per-pair tile counts.
+int run_prefill(const paq_desc* d, const void* query, void* out, const void* key_cache,
+                const void* value_cache, const float* k_scale, const float* v_scale,
+                const int32_t* block_table, const int32_t* cum_q, const int32_t* past_lens,
+                const int32_t* cum_q_host, const int32_t* past_lens_host, float softmax_scale,
+                int padded_mql, void* stream) {
   paq_plan p;
   int rc = plan_prefill(d, cum_q_host, past_lens_host, &p);
   if (rc) return rc;
   if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  if (padded_mql > 0 && padded_mql < p.max_query_len)
+    return fail(PAQ_ERR_INVALID_ARG,
+                "max_query_len %d is below the exact maximum %d: rows would be left unwritten",
+                padded_mql, p.max_query_len);
   rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
                            cum_q, past_lens);
   if (rc) return rc;
@@ -474,10 +609,48 @@ int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
                               block_table, cum_q, past_lens, softmax_scale, p);
   hipStream_t st = (hipStream_t)stream;
   if (p.path == PAQ_PATH_PREFILL) {
-    a.pf_ntq = paq::prefill_uniform_tiles(cum_q_host, d->batch, d->num_heads / d->kv_num_heads);
+    const int group = d->num_heads / d->kv_num_heads;
+    if (padded_mql > 0) {
+      const int tok = paq::prefill_tokens_per_workgroup(group);
+      const long ntq = ((long)padded_mql + tok - 1) / tok;
+      const long pairs = (long)d->kv_num_heads * d->batch;
+      const long grid = 8 * ((pairs + 7) / 8) * ntq;
+      if (grid > 0x7fffffffL) return fail(PAQ_ERR_UNSUPPORTED, "padded prefill grid too large");
+      a.pf_ntq = (int)ntq;
+      a.grid_x = (int)grid;
+    } else {
+      a.pf_ntq = paq::prefill_uniform_tiles(cum_q_host, d->batch, group);
+    }
     return launched(paq::launch_prefill_mfma(a, st), "prefill (MFMA)");
   }
   return launched(paq::launch_decode_f32(a, st), "prefill (fp32)");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
+                           const void* key_cache, const void* value_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* cum_q,
+                           const int32_t* past_lens, const int32_t* cum_q_host,
+                           const int32_t* past_lens_host, float softmax_scale,
+                           void* stream) {
+  return run_prefill(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
+                     past_lens, cum_q_host, past_lens_host, softmax_scale, 0, stream);
+}
+
+int32_t paged_attn_prefill_padded(const paq_desc* d, const void* query, void* out,
+                                  const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_table, const int32_t* cum_q,
+                                  const int32_t* past_lens, const int32_t* cum_q_host,
+                                  const int32_t* past_lens_host, float softmax_scale,
+                                  int32_t max_query_len, void* stream) {
+  if (max_query_len < 1) return fail(PAQ_ERR_INVALID_ARG, "max_query_len %d < 1", max_query_len);
+  return run_prefill(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
+                     past_lens, cum_q_host, past_lens_host, softmax_scale, max_query_len, stream);
 }
 
 int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,

@@ -273,6 +273,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int q0 = a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - q0;
   const int tok0 = qt * TOK;
+  if (tok0 >= qlen) return;            // a padded grid's tile past the new rows
   const int past = a.past_lens[b];
   const int H = a.num_heads, hkv = a.hkv, bs = a.block_size, lbs = a.block_size_log2;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -420,17 +421,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   const int my_tok = min(tok0 + wave * TPW + n / G, qlen - 1);      // clamp padded rows
   const int hq = h * G + (n % G);
   const TQ* qrow = reinterpret_cast<const TQ*>(a.query) + ((size_t)(q0 + my_tok) * H + hq) * D;
-  float Mh = 1.f;
+  // per-channel scales: M_h = 2^e >= max|s| (finite for every finite scale),
+  // q' = q * s / M_h with s / M_h = ldexp(s, -e) exact; the score factor
+  // keeps softmax_scale * M_h (per-head scales: softmax_scale * s) and is
+  // clamped finite (score_factor_log2)
+  int e_h = 0;
   if constexpr (SM == SCALE_CHANNEL) {
     float smax = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) smax = fmaxf(smax, fabsf(a.k_scale[h * D + lane + 64 * i]));
-    smax = wave_max(smax);
-    int ex;
-    const float fr = frexpf(smax, &ex);
-    Mh = (smax == 0.f) ? 1.f : ldexpf(1.f, fr == 0.5f ? ex - 1 : ex);
+    e_h = scale_exponent(wave_max(smax));
   }
-  const float invM = 1.f / Mh;
   kvec qop[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -439,15 +440,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float v = to_f32(e[j]);
-      if constexpr (SM == SCALE_CHANNEL) v *= a.k_scale[h * D + 16 * kk + 8 * eta + j] * invM;
+      if constexpr (SM == SCALE_CHANNEL) v *= ldexpf(a.k_scale[h * D + 16 * kk + 8 * eta + j], -e_h);
       qop[kk][j] = (TK)v;
     }
   }
-  const float sk = (SM == SCALE_CHANNEL) ? Mh : a.k_scale[h];
-  const float c2 = a.softmax_scale * sk * kLog2e;
+  const float c2 = (SM == SCALE_CHANNEL)
+                       ? score_factor_log2(a.softmax_scale, e_h, 1.f)
+                       : fminf(fmaxf(a.softmax_scale * a.k_scale[h] * kLog2e, 0x1p-126f),
+                               0x1.fffffep127f);
   const int row_lim = past + my_tok;              // last key this query column sees
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // running maximum of the raw scores (lazily refreshed), the same in log2
+  // units for the fast exponent form, and the running sum
+  float m_run = -INFINITY, m_log = -INFINITY, l_run = 0.f;
   f32x16 o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
@@ -471,10 +476,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   };
   // Causal mask of tile t (only where it crosses this wave's diagonal; the
   // first row is clamped like the rows themselves, so a wave of padded rows
-  // masks the keys past the end too), then the lazy running maximum in log2
-  // units: the accumulators are rescaled only when a score exceeds it by more
-  // than kPfSlack (the difference is exact near m_run, where m_run + kPfSlack
-  // might round up).
+  // masks the keys past the end too), then the lazy running maximum of the
+  // raw scores: the accumulators are rescaled only when a score exceeds it by
+  // more than kPfSlack in log2 units.  The gap is formed on the raw scores
+  // and scaled afterwards (exact near the maximum, and it cannot overflow).
   auto mask_and_max = [&](int t, f32x16 (&s)[2]) {
     const int key0 = t * kBN;
     if (key0 + kBN - 1 > past + min(tok0 + wave * TPW, qlen - 1)) {
@@ -490,11 +495,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) lm = fmaxf(lm, s[st][r]);
-    lm *= c2;
-    if (__ballot(lm - m_run > kPfSlack)) {
+    if (__ballot((lm - m_run) * c2 > kPfSlack)) {
       const float m_new = fmaxf(m_run, fmaxf(lm, __shfl_xor(lm, 32, 64)));
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = fast_exp2((m_run - m_new) * c2);
       m_run = m_new;
+      m_log = m_new * c2;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NDT; ++i) o[i] *= alpha;
@@ -503,13 +508,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   // P' = 2^7 * 2^(s*c2 - m) in fp16, in the PV B-operand layout (chunk c =
   // regs 8c..8c+7), and partial sums of the same fp16 values, two per dot.
   auto exps = [&](const f32x16 (&s)[2], f16x8 (&p)[4], float (&lp)[4], bool huge) {
-    const float bias = kPfPScaleLog2 - m_run;
+    const float bias = kPfPScaleLog2 - m_log;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         p[2 * st + (r >> 3)][r & 7] =
-            huge ? (f16)fast_exp2(huge_score_arg(s[st][r], c2, m_run, kPfPScaleLog2))
+            huge ? (f16)fast_exp2(safe_score_arg(s[st][r], m_run, c2, kPfPScaleLog2))
                  : (f16)fast_exp2(fmaf(s[st][r], c2, bias));
     const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
 #pragma unroll
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
                      f16x8 (&p)[4], float (&lp)[4]) {
     constexpr bool QK = decltype(do_qk)::value;
     constexpr int NM = 2 * NKK;                     // products (16 for D = 128)
-    const float bias = kPfPScaleLog2 - m_run;
+    const float bias = kPfPScaleLog2 - m_log;
     const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
     const uint8_t* k0p = lds[(t + 1) & 1] + n * Geo::KROW + 16 * eta;
     auto kaddr = [&](int i) { return k0p + (i & 1) * 32 * Geo::KROW + 32 * (i >> 1); };
@@ -646,7 +651,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       phase_a(std::true_type{}, t, s_cur, s_next, p, lp);
     else
       phase_a(std::false_type{}, t, s_cur, s_next, p, lp);
-    if (__builtin_expect(__ballot(fabsf(m_run) > kHugeScoreLog2) != 0, 0))
+    if (__builtin_expect(__ballot(!(fabsf(m_log) <= kHugeScoreLog2)) != 0, 0))
       exps(s_cur, p, lp, true);
     l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     phase_b(t, p, rk, rv, tbB, tbA);

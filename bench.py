@@ -2,17 +2,22 @@
 """Throughput of the paged quantized-KV attention path on one MI355X.
 
 One step = the whole hot path over one batch: host planning, kv_quant_append
-of the step's new tokens, then paged_attn_decode (single pass, or split-KV +
-combine) or paged_attn_prefill.  Inputs are seeded synthetic workloads
-(workloads/), resident in HBM before the timed region.  The KV cache is
-rotated over several pools (>= ~1 GiB in total) so that every step reads it
-cold from HBM rather than from the 256 MB Infinity Cache.
+of the step's new tokens, then paged_attn_decode or paged_attn_prefill.
+Inputs are seeded synthetic workloads (workloads/), resident in HBM before the
+timed region.  The KV cache is rotated over several pools (>= ~1.1 GiB in
+total) so that every step reads it cold from HBM rather than from the 256 MB
+Infinity Cache.
 
-Prints one JSON line.  `value` is the decode KV-cache bandwidth (algorithmic
-KV bytes read per step / step time, GB/s) for decode workloads, or the
-algorithmic MFMA rate (TFLOP/s, unmasked causal pairs only) for prefill.
-`roofline` is measured for the dominant kernel (the attention call) with HIP
-events on its stream; `cpu_baseline` times the fp64 oracle on the host cores.
+Prints one JSON line.  The headline (`value`, `roofline`, `cpu_baseline`) is
+the --workload (default int8_decode, the GQA INT8 decode the metric is quoted
+on): decode KV-cache bandwidth (algorithmic KV bytes read per step / step
+time, GB/s), or the algorithmic MFMA rate (TFLOP/s, unmasked causal pairs
+only) for prefill.  `roofline` is measured for the attention call with HIP
+events on its stream.  Unless --only is given, `configs` holds the same
+measurement for the other four workloads (tiny_decode's latency in us
+included) and `ablations` the partition and grid comparisons: single pass
+against the automatic split on the two decode workloads, and the exact
+prefill grid against one sized from token_count - batch + 1.
 """
 
 import argparse
@@ -69,6 +74,11 @@ def parse():
     ap.add_argument("--rotary", action="store_true",
                     help="the step's append is kv_quant_append_rotary (rotary embedding of "
                          "the new query and key rows over all head_size channels)")
+    ap.add_argument("--padded-grid", action="store_true",
+                    help="prefill: size the grid from token_count - batch + 1 for every "
+                         "(sequence, kv head) pair (paged_attn_prefill_padded)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the --workload alone (no configs / ablations)")
     return ap.parse_args()
 
 
@@ -146,11 +156,30 @@ def cpu_kernel(w, g, desc, calls=5):
             "tokens_per_s": round(int((w.q_lens > 0).sum()) / sec, 1)}
 
 
+def host_stream_gbs(threads, nbytes=2 ** 31):
+    """Streaming-read bandwidth of the host with `threads` threads (numpy sums
+    over disjoint slices of a 2 GiB array; numpy releases the GIL in them):
+    the roofline of the host decode."""
+    import concurrent.futures
+    a = np.ones(nbytes // 4, np.float32)
+    parts = np.array_split(a, threads)
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(np.sum, parts))                      # touch / warm
+        best = 0.0
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(np.sum, parts))
+            best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
+    return round(best, 2)
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, on the host cores, over a bounded sample of the
     same workload: its sequences one after another (cycling through the batch)
     until the time budget is spent; each costs one oracle quant_append of the
-    sequence's new rows plus its oracle attention."""
+    sequence's new rows plus its oracle attention.  Each sequence gets a pool
+    of its own blocks only (gathered before timing), so the oracle's append
+    copies that sequence's cache, not the whole batch's."""
     import threadpoolctl
     from oracle import attention, quant
     from tests.oracle_cases import f32, oracle_caches
@@ -161,15 +190,20 @@ def cpu_baseline(w, seconds):
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     active = [b for b in range(w.batch) if w.q_lens[b] > 0]
+    pools = {}
+    for b in active:
+        nb = -(-int(w.kv_lens[b]) // w.block_size)
+        blocks = w.block_table[b, :nb]
+        pools[b] = (kc[blocks], vc[blocks], np.arange(nb, dtype=np.int32)[None])
     done_kv = done_flops = done_tok = nseq = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         b = active[nseq % len(active)]
         r0, r1 = int(w.cum_q[b]), int(w.cum_q[b + 1])
         cq = np.array([0, r1 - r0], np.int32)
-        bt = w.block_table[b:b + 1]
         pl = w.past_lens[b:b + 1]
-        kc2, vc2 = quant.quant_append(kc, vc, kin[r0:r1], vin[r0:r1], w.k_scale, w.v_scale,
+        pk, pv, bt = pools[b]
+        kc2, vc2 = quant.quant_append(pk, pv, kin[r0:r1], vin[r0:r1], w.k_scale, w.v_scale,
                                       bt, cq, pl, w.kv_format)
         attention.paged_attention(q[r0:r1], kc2, vc2, w.k_scale, w.v_scale, bt, cq, pl,
                                   w.kv_format)
@@ -181,7 +215,8 @@ def cpu_baseline(w, seconds):
     el = time.perf_counter() - t0
     res = {"cores": int(threads), "kind": "oracle",
            "sample": "%d sequences of %s (cycling through the batch; fp64 oracle "
-                     "quant_append + attention per sequence), %.1f s wall" % (nseq, w.name, el),
+                     "quant_append of the sequence's new rows into a pool of its own blocks, "
+                     "then its attention), %.1f s wall" % (nseq, w.name, el),
            "tokens_per_s": round(done_tok / el, 3)}
     if w.kind == "decode":
         res.update({"value": round(done_kv / el / 1e9, 5), "unit": "GB/s"})
@@ -350,31 +385,25 @@ def sleep_rate(stream):
     return max(rates)
 
 
-def main():
-    args = parse()
-    if args.summarize_stats:
-        summarize_stats(args)
-        return
-    if args.summarize_pmc:
-        summarize_pmc(args)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
-        sys.exit(2)
+_WORKLOADS = {}          # workloads built so far (the ablations reuse them)
 
+
+def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, warm=True,
+            append_loop=True):
+    """Time `steps` steps (append + attention) of workload `name` after
+    `warmup` untimed ones; returns the measurement as a dict, plus the
+    workload, one filled Device and the descriptor (for the CPU figures)."""
     import torch
     import attention_paged_quantized_amd as paq
     import workloads
     from tests.gpu_cases import Device, desc_for
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    paq.lib()
-    w = workloads.make(args.workload)
+    if name not in _WORKLOADS:
+        _WORKLOADS[name] = workloads.make(name)
+    w = _WORKLOADS[name]
     kind = w.kind
-    S = w.num_splits if args.splits is None else args.splits
+    S = w.num_splits if splits is None else splits
     T = w.token_count
     print("[bench] workload %s: batch %d, tokens %d, kv bytes %.1f MB" %
           (w.name, w.batch, T, kv_bytes(w) / 1e6), file=sys.stderr, flush=True)
@@ -387,19 +416,22 @@ def main():
           flush=True)
 
     desc = desc_for(w, T)
-    if args.rotary:
+    if rotary:
         rcos, rsin = workloads.rope_tables(int(w.kv_lens.max()) + 1, w.head_size)
         rcos, rsin = torch.from_numpy(rcos).to(dev), torch.from_numpy(rsin).to(dev)
     kin = w.new_key.to(dev)
     vin = w.new_value.to(dev)
     outs = [torch.empty_like(g.query) for g in devs]
     ws = None
+    plan = None
     if kind == "decode":
+        plan = paq.paq_plan_decode(desc, w.cum_q, w.past_lens, S)
         nbytes = paq.paged_attn_decode_workspace_size(desc, w.cum_q, w.past_lens, S)
         if nbytes:
-            ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=dev)
+            ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    if args.sparse:
+    heuristic_mql = T - w.batch + 1
+    if sparse:
         if kind != "decode":
             sys.exit("--sparse applies to decode workloads")
         nbk = -(-(w.past_lens + 1) // w.block_size)
@@ -411,13 +443,13 @@ def main():
         sel_d, num_d = torch.from_numpy(sel_np).to(dev), torch.from_numpy(num_np).to(dev)
         nbytes = paq.paged_attn_decode_sparse_workspace_size(desc, w.cum_q, w.past_lens, num_np,
                                                              sel_np.shape[1], S)
-        ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=dev)
+        ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
         # selected keys: whole blocks, the last one up to kv_len
         sel_keys = [sum(min(w.block_size, int(w.past_lens[b]) + 1 - w.block_size * x) for x in r)
                     for b, r in enumerate(rows)]
 
     def attention(g, out):
-        if kind == "decode" and args.sparse:
+        if kind == "decode" and sparse:
             paq.paged_attn_decode_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                          g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
                                          sel_d, num_d, num_np, 0.0, S, ws, stream)
@@ -425,13 +457,17 @@ def main():
             paq.paged_attn_decode(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                   g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0, S,
                                   ws, stream)
+        elif padded:
+            paq.paged_attn_prefill_padded(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                          g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
+                                          heuristic_mql, 0.0, stream)
         else:
             paq.paged_attn_prefill(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                    g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0,
                                    stream)
 
     def append(g):
-        if args.rotary:
+        if rotary:
             paq.kv_quant_append_rotary(desc, w.kv_in_dtype, g.query, kin, vin, g.kc, g.vc,
                                        g.k_scale, g.v_scale, g.block_table, g.cum_q, g.past,
                                        w.cum_q, w.past_lens, rcos, rsin, w.head_size, False,
@@ -484,37 +520,155 @@ def main():
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
     kern_sorted = sorted(kern_ms)
-    # the append on its own: per-call events over the same pools, outside the
-    # timed steps (its events would add to their time)
-    aevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    hold(args.steps)
-    for i, (e0, e1) in enumerate(aevs):
-        e0.record(stream)
-        append(devs[i % pools])
-        e1.record(stream)
-    torch.cuda.synchronize()
-    app_avg = sum(a.elapsed_time(b) for a, b in aevs) / len(aevs)
+    app_avg = None
+    if append_loop:
+        # the append on its own: per-call events over the same pools, outside
+        # the timed steps (its events would add to their time)
+        aevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        hold(args.steps)
+        for i, (e0, e1) in enumerate(aevs):
+            e0.record(stream)
+            append(devs[i % pools])
+            e1.record(stream)
+        torch.cuda.synchronize()
+        app_avg = sum(a.elapsed_time(b) for a, b in aevs) / len(aevs)
 
     # warm (cache-resident) reference: the same pool every call, per-call events
     warm_ms = None
-    for i in range(0 if args.skip_warm else 5):
-        attention(devs[0], outs[0])
-    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(0 if args.skip_warm else 20)]
-    torch.cuda.synchronize()
-    hold(len(wev))
-    for e0, e1 in wev:
-        e0.record(stream)
-        attention(devs[0], outs[0])
-        e1.record(stream)
-    torch.cuda.synchronize()
-    if wev:
+    if warm and not args.skip_warm:
+        for i in range(5):
+            attention(devs[0], outs[0])
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        torch.cuda.synchronize()
+        hold(len(wev))
+        for e0, e1 in wev:
+            e0.record(stream)
+            attention(devs[0], outs[0])
+            e1.record(stream)
+        torch.cuda.synchronize()
         warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
 
-    # plain streaming copy of 1 GiB for context (read + write bytes / time); with
+    r = {"workload": w.name, "ms_per_step": round(ms_step, 6)}
+    cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
+           "kv_num_heads": w.kv_num_heads, "head_size": w.head_size,
+           "block_size": w.block_size, "kv_format": w.kv_format, "scale_mode": w.scale_mode,
+           "q_dtype": w.q_dtype, "token_count": T, "kv_pools": pools}
+    p10p90 = [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
+              round(kern_sorted[9 * len(kern_ms) // 10] * 1e3, 3)]
+    if kind == "decode":
+        kvb = kv_bytes(w)
+        if sparse:
+            act = w.q_lens > 0
+            kvb = int(sum(k for k, a in zip(sel_keys, act) if a)) * w.kv_num_heads * 2 * \
+                w.cache_head_size
+        act = int((w.q_lens > 0).sum())
+        r.update({"value": round(kvb / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s",
+                  "tokens_per_s": round(act / (ms_step / 1e3), 1),
+                  "hbm_frac": round(kvb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
+        cfg.update({"num_splits": S, "path": paq.PATHS[plan.path],
+                    "parts": plan.parts, "keys_per_group": plan.keys_per_group,
+                    "kv_bytes_per_step": kvb, "max_kv_len": int(w.kv_lens.max())})
+        achieved = kvb / (kern_avg / 1e3) / 1e9
+        traffic = None if sparse else counters(w.name, "decode")
+        call = "decode_stream_kernel" if plan.path in (1, 2, 7) else \
+            "attn_f32_kernel" + (" + combine_kernel" if plan.path == 4 else "")
+        r["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "kernel": ("paged_attn_decode_sparse call (sparse_compact_kernel + %s)"
+                                    if sparse else "paged_attn_decode call (%s)") % call,
+                         "kernel_us_avg": round(kern_avg * 1e3, 3),
+                         "kernel_us_p10_p90": p10p90,
+                         "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
+                         "algorithmic_bytes_per_launch": kvb}
+    else:
+        fl = prefill_flops(w)
+        peak = MFMA_PEAK_TFLOPS[w.q_dtype]
+        r.update({"value": round(fl / (ms_step / 1e3) / 1e12, 3), "unit": "TFLOP/s",
+                  "tokens_per_s": round(T / (ms_step / 1e3), 1)})
+        achieved = fl / (kern_avg / 1e3) / 1e12
+        r["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                         "traffic": None if padded else counters(w.name, "prefill"),
+                         "kernel": "paged_attn_prefill%s call (prefill_mfma_kernel)" %
+                                   ("_padded" if padded else ""),
+                         "kernel_us_avg": round(kern_avg * 1e3, 3),
+                         "kernel_us_p10_p90": p10p90,
+                         "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
+                         "algorithmic_flops_per_launch": fl}
+        cfg.update({"max_query_len": int(w.q_lens.max()), "causal": True,
+                    "grid": "token_count - batch + 1 = %d for every pair" % heuristic_mql
+                            if padded else "exact"})
+    r["config"] = cfg
+    if app_avg is not None:
+        ab = append_bytes(w, T, rotary)
+        r["append"] = {"kernel": "rotary_append_kernel" if rotary else "quant_append_kernel",
+                       "bound": "hbm", "us_avg": round(app_avg * 1e3, 3),
+                       "algorithmic_bytes": ab,
+                       "achieved": round(ab / (app_avg / 1e3) / 1e9, 2), "unit": "GB/s",
+                       "frac": round(ab / (app_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "traffic": counters(w.name, "rotary_append_kernel" if rotary
+                                           else "quant_append_kernel")}
+    if sparse:
+        cfg["sparse"] = "2-block local window + every 3rd earlier block; %d of %d KV bytes" % (
+            kvb, kv_bytes(w))
+    keep = devs[0]
+    del devs, outs, ws
+    torch.cuda.empty_cache()
+    return r, w, keep, desc
+
+
+def summary(r):
+    """The per-configuration line of a measurement."""
+    rf = r["roofline"]
+    out = {"ms_per_step": r["ms_per_step"], "value": r["value"], "unit": r["unit"],
+           "tokens_per_s": r["tokens_per_s"], "kernel_us_avg": rf["kernel_us_avg"],
+           "kernel_us_p10_p90": rf["kernel_us_p10_p90"], "achieved": rf["achieved"],
+           "roofline_unit": rf["unit"], "bound": rf["bound"], "frac": rf["frac"],
+           "traffic": rf["traffic"], "kernel": rf["kernel"], "config": r["config"]}
+    if r["config"]["workload"] == "tiny_decode":
+        out["latency_us"] = rf["kernel_us_avg"]
+    if "append" in r:
+        out["append_us"] = r["append"]["us_avg"]
+    return out
+
+
+def main():
+    args = parse()
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_paged_quantized_amd as paq
+
+    torch.cuda.set_device(0)
+    paq.lib()
+    r, w, g0, desc = measure(args, args.workload, splits=args.splits, padded=args.padded_grid,
+                             rotary=args.rotary, sparse=args.sparse)
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16"}.get(w.q_dtype, "f16"),
+              "data": "synthetic (seeded; workloads/%s)" % w.name}
+    for k in ("value", "unit", "tokens_per_s", "hbm_frac", "roofline", "config", "append"):
+        if k in r:
+            result[k] = r[k]
+
+    # the copy rate of this GPU for context (read + write bytes / time); with
     # --calib-copy also the 256 MiB copy whose counters scale FETCH/WRITE_SIZE
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
     src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -524,77 +678,47 @@ def main():
         dst.copy_(src)
     c1.record(stream)
     torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    result["hbm_copy_GBs"] = round(2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9, 1)
     if args.calib_copy:
         for _ in range(3):
             torch.neg(src[:CALIB_ELEMS], out=dst[:CALIB_ELEMS])
         torch.cuda.synchronize()
     del src, dst
 
-    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-              "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
-              "vs_baseline": None, "dtype": "f16" if w.q_dtype != "bf16" else "bf16",
-              "data": "synthetic (seeded; workloads/%s)" % w.name}
-    if w.q_dtype == "f32":
-        result["dtype"] = "f32"
-    cfg = {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
-           "kv_num_heads": w.kv_num_heads, "head_size": w.head_size,
-           "block_size": w.block_size, "kv_format": w.kv_format, "scale_mode": w.scale_mode,
-           "q_dtype": w.q_dtype, "token_count": T, "kv_pools": pools}
-    if kind == "decode":
-        kvb = kv_bytes(w)
-        if args.sparse:
-            act = w.q_lens > 0
-            kvb = int(sum(k for k, a in zip(sel_keys, act) if a)) * w.kv_num_heads * 2 * \
-                w.cache_head_size
-        act = int((w.q_lens > 0).sum())
-        result.update({"value": round(kvb / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s",
-                       "tokens_per_s": round(act / (ms_step / 1e3), 1),
-                       "hbm_frac": round(kvb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
-        cfg.update({"num_splits": S, "kv_bytes_per_step": kvb,
-                    "max_kv_len": int(w.kv_lens.max())})
-        achieved = kvb / (kern_avg / 1e3) / 1e9
-        traffic = None if args.sparse else counters(w.name, "decode")
-        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                              "kernel": ("paged_attn_decode_sparse call (sparse_compact_kernel + %s)"
-                                         if args.sparse else "paged_attn_decode call (%s)") %
-                                        ("decode_stream_kernel" + (" + combine_kernel" if S > 1 else "")),
-                              "kernel_us_avg": round(kern_avg * 1e3, 3),
-                              "kernel_us_p10_p90": [round(kern_sorted[len(kern_ms) // 10] * 1e3, 3),
-                                                    round(kern_sorted[9 * len(kern_ms) // 10] * 1e3, 3)],
-                              "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
-                              "algorithmic_bytes_per_launch": kvb}
-    else:
-        fl = prefill_flops(w)
-        peak = MFMA_PEAK_TFLOPS[w.q_dtype]
-        result.update({"value": round(fl / (ms_step / 1e3) / 1e12, 3), "unit": "TFLOP/s",
-                       "tokens_per_s": round(T / (ms_step / 1e3), 1)})
-        achieved = fl / (kern_avg / 1e3) / 1e12
-        result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                              "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                              "traffic": counters(w.name, "prefill"),
-                              "kernel": "paged_attn_prefill call (prefill_mfma_kernel)",
-                              "kernel_us_avg": round(kern_avg * 1e3, 3),
-                              "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
-                              "algorithmic_flops_per_launch": fl}
-        cfg.update({"max_query_len": int(w.q_lens.max()), "causal": True})
-    result["config"] = cfg
-    ab = append_bytes(w, T, args.rotary)
-    result["append"] = {"kernel": "rotary_append_kernel" if args.rotary else "quant_append_kernel",
-                        "bound": "hbm", "us_avg": round(app_avg * 1e3, 3),
-                        "algorithmic_bytes": ab,
-                        "achieved": round(ab / (app_avg / 1e3) / 1e9, 2), "unit": "GB/s",
-                        "frac": round(ab / (app_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "traffic": counters(w.name, "rotary_append_kernel" if args.rotary
-                                            else "quant_append_kernel")}
-    result["hbm_copy_GBs"] = round(copy_gbs, 1)
-    if args.sparse:
-        cfg["sparse"] = "2-block local window + every 3rd earlier block; %d of %d KV bytes" % (
-            kvb, kv_bytes(w))
-    if kind == "decode" and not args.no_cpu_baseline and not args.sparse:
-        result["cpu_kernel"] = cpu_kernel(w, devs[0], desc)
+    if not args.only and not args.sparse and not args.rotary:
+        # every configuration, then the ablations (short timings each)
+        configs = {}
+        for name in ("tiny_decode", "int8_decode", "int4_long", "int8_prefill", "fp8_prefill"):
+            if name == w.name:
+                configs[name] = summary(r)
+                continue
+            cr = measure(args, name, warm=False)[0]
+            configs[name] = summary(cr)
+        result["configs"] = configs
+        abl = {}
+        for label, name, kw in (
+                ("int8_decode single pass (num_splits 1)", "int8_decode", {"splits": 1}),
+                ("int4_long single pass (num_splits 1)", "int4_long", {"splits": 1}),
+                ("int8_prefill grid from token_count - batch + 1", "int8_prefill",
+                 {"padded": True}),
+                ("fp8_prefill grid from token_count - batch + 1", "fp8_prefill",
+                 {"padded": True})):
+            ar = measure(args, name, warm=False, append_loop=False, **kw)[0]
+            s = summary(ar)
+            ref = configs[name]
+            s["time_vs_default"] = round(s["kernel_us_avg"] / ref["kernel_us_avg"], 3)
+            abl[label] = s
+        result["ablations"] = abl
+
+    if w.kind == "decode" and not args.no_cpu_baseline and not args.sparse:
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") \
+            else os.cpu_count()
+        threads = max(1, min(16, threads))
+        ck = cpu_kernel(w, g0, desc)
+        ck["host_stream_GBs"] = host_stream_gbs(threads)
+        ck["frac_of_host_stream"] = round(ck["value"] / ck["host_stream_GBs"], 4)
+        result["cpu_kernel"] = ck
+    del g0
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (%.0f s budget)" % args.cpu_seconds,
               file=sys.stderr, flush=True)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define PAQ_ABI_VERSION 1
+#define PAQ_ABI_VERSION 2
 
 enum paq_status {
   PAQ_OK = 0,
@@ -93,12 +93,16 @@ enum paq_scale_mode { PAQ_SCALE_PER_CHANNEL = 0, PAQ_SCALE_PER_HEAD = 1 };
 /* Which kernels a decode call runs (see paq_plan_decode). */
 enum paq_path {
   PAQ_PATH_NONE = 0,         /* no rows: nothing is launched                    */
-  PAQ_PATH_SINGLE = 1,       /* one pass per (sequence, kv head), 16-bit MFMA   */
-  PAQ_PATH_SPLIT = 2,        /* split-KV chunks + log-sum-exp combine, MFMA     */
+  PAQ_PATH_SINGLE = 1,       /* one part per (sequence, head group), MFMA       */
+  PAQ_PATH_SPLIT = 2,        /* num_splits block-aligned chunks per sequence,   */
+                             /* merged in the same launch, MFMA                 */
   PAQ_PATH_F32_SINGLE = 3,   /* portable fp32 kernel, one pass                  */
   PAQ_PATH_F32_SPLIT = 4,    /* portable fp32 kernel, split-KV + combine        */
   PAQ_PATH_PREFILL = 5,      /* MFMA prefill tiles                              */
-  PAQ_PATH_F32_PREFILL = 6   /* portable fp32 kernel, one query row per group   */
+  PAQ_PATH_F32_PREFILL = 6,  /* portable fp32 kernel, one query row per group   */
+  PAQ_PATH_BALANCED = 7      /* length-balanced: every workgroup streams an     */
+                             /* equal share of all tiles; merged in the same    */
+                             /* launch, MFMA                                    */
 };
 
 /* Shape/format description shared by all calls. */
@@ -116,17 +120,27 @@ typedef struct paq_desc {
   int32_t scale_mode;         /* enum paq_scale_mode                           */
 } paq_desc;
 
-/* Host-side plan of a call (introspection; the calls compute it themselves). */
+/* Host-side plan of a call (introspection; the calls compute it themselves,
+ * and launch exactly what it describes). */
 typedef struct paq_plan {
   int32_t max_query_len;    /* exact max_b q_len_b, from the host cum_q        */
   int32_t max_kv_len;       /* max_b past_b + q_len_b over sequences with rows */
   int32_t active_seqs;      /* sequences with q_len > 0                        */
   int32_t work_units;       /* active_seqs * kv_num_heads                      */
-  int32_t num_splits;       /* KV chunks per sequence (1 = single pass)        */
+  int32_t num_splits;       /* decode: KV chunks per sequence (1 = single      */
+                            /* pass, 0 = length-balanced)                      */
   int32_t path;             /* enum paq_path                                   */
   int32_t grid_x, grid_y, grid_z; /* launch grid of the main kernel            */
-  int32_t reserved;
-  uint64_t workspace_bytes; /* device workspace the call needs (split decode)  */
+  int32_t waves_per_group;  /* waves (64 lanes) per workgroup of it            */
+  int32_t parts;            /* MFMA decode: PAQ_PATH_SPLIT: sequences x parts  */
+                            /* of a sequence; PAQ_PATH_BALANCED: workgroups    */
+  int32_t parts_per_seq;    /* PAQ_PATH_SPLIT: parts of every sequence         */
+  int32_t chunks_per_part;  /* PAQ_PATH_SPLIT: consecutive chunks per part     */
+  int32_t keys_per_group;   /* PAQ_PATH_BALANCED: keys each workgroup streams  */
+                            /* (at most)                                       */
+  int64_t total_tiles;      /* PAQ_PATH_BALANCED: 32-key tiles of all          */
+                            /* (sequence, head group) pairs                    */
+  uint64_t workspace_bytes; /* device workspace the call needs                 */
 } paq_plan;
 
 /* ABI version of the loaded library (PAQ_ABI_VERSION). */
@@ -139,11 +153,20 @@ const char* paq_status_string(int32_t status);
 const char* paq_last_error(void);
 
 /* Plan a decode call without launching anything (pure host code, usable
- * without a GPU).  num_splits: 0 = automatic (split when the work units
- * under-fill num_cus compute units and a sequence has more than one block,
- * mirroring the flash-decoding rule of "GQA GEMV decode", section 2), 1 = single
- * pass, > 1 = that many block-aligned chunks per sequence.  num_cus <= 0
- * queries the current device.  Returns a status; fills *plan on success. */
+ * without a GPU).  num_splits:
+ *   1  single pass: one workgroup per (sequence, head group);
+ *   S > 1  S block-aligned chunks per sequence (flash decoding, "GQA GEMV
+ *      decode", section 2), grouped into about one workgroup per compute unit;
+ *   -N length-balanced over N workgroups (N <= 256): the 32-key tiles of all
+ *      (sequence, head group) pairs are dealt out in N equal contiguous runs,
+ *      so every workgroup streams the same bytes whatever the lengths;
+ *   0  automatic: length-balanced over about one workgroup per compute unit
+ *      while the (sequence, head group) pairs alone would give fewer than four
+ *      per compute unit (the flash-decoding rule of the same section, which
+ *      splits when batch x heads under-fills the machine), else single pass.
+ * Split and balanced calls merge partial results inside the same launch.
+ * num_cus <= 0 plans for the current device (256 compute units when no device
+ * is visible).  Returns a status; fills *plan on success. */
 int32_t paq_plan_decode(const paq_desc* d, const int32_t* cum_q_host,
                         const int32_t* past_lens_host, int32_t num_splits,
                         int32_t num_cus, paq_plan* plan);
@@ -185,6 +208,24 @@ int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,
                            const int32_t* past_lens, const int32_t* cum_q_host,
                            const int32_t* past_lens_host, float softmax_scale,
                            void* stream);
+
+/* paged_attn_prefill with the launch grid sized from a caller-supplied
+ * max_query_len instead of the exact one: every (sequence, kv head) pair gets
+ * ceil(max_query_len / tile) query tiles, and tiles past a sequence's new
+ * rows exit at once.  This is the interface "PagedAttention FA path: exact
+ * max_query_len" (section 1) shows before its fix, where the value was
+ * token_count - batch + 1; a value below the exact maximum would leave rows
+ * unwritten, so it is refused (PAQ_ERR_INVALID_ARG) rather than dropping
+ * them.  For measuring what grid sizing costs; paged_attn_prefill, with its
+ * exact grid, is the call to use.  fp32 queries (one workgroup per row) take
+ * the same path as paged_attn_prefill.  Otherwise identical to it. */
+int32_t paged_attn_prefill_padded(const paq_desc* d, const void* query, void* out,
+                                  const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_table, const int32_t* cum_q,
+                                  const int32_t* past_lens, const int32_t* cum_q_host,
+                                  const int32_t* past_lens_host, float softmax_scale,
+                                  int32_t max_query_len, void* stream);
 
 /* Quantize rows cum_q[b]..cum_q[b+1]-1 of key/value (token_count, kv_num_heads,
  * head_size; dtype kv_in_dtype) and store row i of sequence b at position

@@ -12,6 +12,7 @@ import torch
 import attention_paged_quantized_amd as paq
 
 POISON = 0x7F          # same poison byte as the oracle-side pools
+COUNTERS = 16384       # int32 arrival counters at the head of a decode workspace
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -76,11 +77,15 @@ class Device:
         desc = desc_for(w, T)
         if kind == "decode":
             nbytes = paq.paged_attn_decode_workspace_size(desc, w.cum_q, w.past_lens, S)
-            ws = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=self.dev) \
+            ws = torch.zeros(max(1, nbytes // 4), dtype=torch.float32, device=self.dev) \
                 if nbytes else None
             paq.paged_attn_decode(desc, self.query, out, self.kc, self.vc, self.k_scale,
                                   self.v_scale, self.block_table, self.cum_q, self.past, w.cum_q,
                                   w.past_lens, softmax_scale, S, ws)
+            if ws is not None:
+                torch.cuda.synchronize()
+                # the arrival counters at the head of the workspace are zero again
+                assert not ws.view(torch.int32)[:COUNTERS].any(), "counters left non-zero"
         else:
             paq.paged_attn_prefill(desc, self.query, out, self.kc, self.vc, self.k_scale,
                                    self.v_scale, self.block_table, self.cum_q, self.past,

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert paq.paq_abi_version() == 1
+    assert paq.paq_abi_version() == paq.ABI_VERSION == 2
     assert paq.paq_status_string(0) == "ok"
     assert "workspace" in paq.paq_status_string(3)
     assert paq.paq_status_string(99) == "unknown status"
@@ -51,33 +51,91 @@ def _cum(qlens):
     return np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
 
 
+COUNTER_BYTES = 16384 * 4      # arrival counters at the head of every decode workspace
+
+
 def test_plan_decode_paths_and_workspace():
     # tiny decode: fp32 queries -> the portable fp32 kernel, one pass
     d = paq.make_desc(3, 2, 4, 2, 64, 16, 24, 8, "f32", "int8", "channel")
     p = paq.paq_plan_decode(d, [0, 1, 2, 2], [37, 100, 0], 0, 256)
     assert (p.max_query_len, p.max_kv_len, p.active_seqs, p.work_units) == (1, 101, 2, 4)
     assert paq.PATHS[p.path] == "f32_single" or paq.PATHS[p.path] == "f32_split"
-    # long INT4 decode with 128 chunks: a workgroup merges its 8 chunks, so the
-    # workspace holds T*H*(S/8)*(D+1) fp32 (aligned)
+    # long INT4 decode with 128 chunks: one wave per pair of INT4 kv heads (a
+    # 128-byte line) -> 4 head groups; 4 sequences x 4 groups = 16 units, so
+    # about one workgroup per CU needs 16 parts of 8 chunks per sequence
     d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
     p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 128, 256)
-    # one wave per chunk and per pair of INT4 kv heads (a 128-byte line), 8 waves
-    # per workgroup: grid (8 / 2, 4, 128 / 8)
-    assert p.num_splits == 128 and (p.grid_x, p.grid_y, p.grid_z) == (4, 4, 16)
-    assert p.workspace_bytes == 4 * 32 * 16 * 128 * 4 + 4 * 32 * 16 * 4
+    assert paq.PATHS[p.path] == "split" and p.num_splits == 128
+    assert (p.parts_per_seq, p.chunks_per_part, p.parts) == (16, 8, 64)
+    assert (p.grid_x, p.grid_y, p.grid_z, p.waves_per_group) == (64 * 4, 1, 1, 8)
+    # workspace: counters, then one partial (D fp32) and one (max, sum) pair per
+    # part and query head
+    slots = 64 * 32
+    al = lambda x: -(-x // 256) * 256
+    assert p.workspace_bytes == COUNTER_BYTES + al(slots * 128 * 4) + al(slots * 2 * 4)
+    # (sizing without a plan of its own uses the device's compute units, or
+    # 256 when no GPU is visible -- as here, and as on an MI355X)
     assert paq.paged_attn_decode_workspace_size(d, _cum([1] * 4), [32768] * 4, 128) == \
         p.workspace_bytes
-    # 256 (sequence, kv head) units fill 256 CUs: automatic choice is one pass
+    # 256 (sequence, kv head) units fill 256 CUs: the automatic choice is one pass
     d = _desc(32, 32, mb=257, nb=6000)
-    p = paq.paq_plan_decode(d, _cum([1] * 32), [2000] * 32, 0, 256)
-    assert p.num_splits == 1 and p.workspace_bytes == 0
-    # 32 units under-fill 256 CUs and sequences are long: automatic split
-    d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
-    p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 0, 256)
-    assert p.num_splits == 16
+    past = [1024 + 96 * b for b in range(32)]
+    p = paq.paq_plan_decode(d, _cum([1] * 32), past, 0, 256)
+    assert paq.PATHS[p.path] == "single" and p.workspace_bytes == 0
+    # under-filled with near-uniform lengths: block-aligned chunks, about two
+    # workgroups per CU (4 sequences x 4 INT4 head groups = 16 units -> 32)
+    d4 = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
+    p = paq.paq_plan_decode(d4, _cum([1] * 4), [32768] * 4, 0, 256)
+    assert paq.PATHS[p.path] == "split" and p.num_splits == 32
+    # under-filled with skewed lengths (longest > 1.5 x mean): the
+    # length-balanced partition over one workgroup per CU, each streaming an
+    # equal share of the 32-key tiles of all (sequence, kv head) pairs; a
+    # workgroup keeps partials for its first and last pieces
+    dk = _desc(4, 4, mb=2000, nb=9000)
+    pk = [30000, 100, 200, 300]
+    p = paq.paq_plan_decode(dk, _cum([1] * 4), pk, 0, 256)
+    assert paq.PATHS[p.path] == "balanced" and p.num_splits == 0
+    total = sum(-(-(x + 1) // 32) for x in pk) * 8
+    assert p.total_tiles == total and p.parts == 256 and p.grid_x == 256
+    assert p.keys_per_group == 32 * -(-total // 256)
+    rows = 2 * 256 * 4                  # slots x query heads per head group
+    assert p.workspace_bytes == COUNTER_BYTES + al(rows * 128 * 4) + al(rows * 2 * 4)
+    # an explicit length-balanced split: -N workgroups
+    p = paq.paq_plan_decode(d, _cum([1] * 32), past, -100, 256)
+    assert paq.PATHS[p.path] == "balanced" and p.parts == 100 and p.grid_x == 100
+    # enough units for the dispatcher alone: one pass, no workspace
+    d = _desc(256, 256, mb=257, nb=60000)
+    p = paq.paq_plan_decode(d, _cum([1] * 256), [2000] * 256, 0, 256)
+    assert paq.PATHS[p.path] == "single" and p.workspace_bytes == 0
     # short sequences are not split
     p = paq.paq_plan_decode(_desc(2, 2), _cum([1, 1]), [10, 100], 0, 256)
-    assert p.num_splits == 1
+    assert p.num_splits == 1 and paq.PATHS[p.path] == "single"
+
+
+@pytest.mark.parametrize("cus", [32, 256, 304])
+def test_plan_decode_split_follows_the_compute_units(cus):
+    """The split partition is sized for the compute units it is planned for,
+    and the plan carries everything the launch uses: parts x chunks per part
+    cover every chunk, the grid is parts x head groups, and the workspace
+    holds a partial for every part and query head."""
+    d = _desc(4, 4, bs=32, nb=4200, mb=1025, fmt="int4")
+    p = paq.paq_plan_decode(d, _cum([1] * 4), [32768] * 4, 128, cus)
+    assert p.parts_per_seq * p.chunks_per_part >= 128
+    assert (p.parts_per_seq - 1) * p.chunks_per_part < 128
+    assert p.parts == 4 * p.parts_per_seq and p.grid_x == 4 * p.parts
+    assert p.grid_x >= min(cus, 4 * 4 * 128) * 0.5
+    al = lambda x: -(-x // 256) * 256
+    slots = p.parts * 32
+    assert p.workspace_bytes == COUNTER_BYTES + al(slots * 128 * 4) + al(slots * 2 * 4)
+
+
+def test_plan_decode_rejects_bad_balanced_requests():
+    d = _desc(2, 2)
+    with pytest.raises(paq.PaqError):
+        paq.paq_plan_decode(d, _cum([1, 1]), [100, 300], -257, 256)      # > 256 workgroups
+    # fewer tiles than workgroups: one workgroup per tile at most
+    p = paq.paq_plan_decode(d, _cum([1, 1]), [10, 40], -200, 256)
+    assert p.parts == p.total_tiles == (1 + 2) * 8
 
 
 def test_plan_prefill_uses_exact_max_query_len():
@@ -194,7 +252,7 @@ def test_decode_specific_checks():
     d = _desc(2, 3)
     assert _call_decode(d, [0, 2, 3], [4, 4]) == paq.PAQ_ERR_INVALID_ARG     # q_len 2
     assert "q_len" in paq.paq_last_error()
-    assert _call_decode(_desc(1, 1), [0, 1], [4], splits=-1) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_decode(_desc(1, 1), [0, 1], [4], splits=-257) == paq.PAQ_ERR_UNSUPPORTED
     # split decode without (or with too small) a workspace
     assert _call_decode(_desc(1, 1), [0, 1], [100], splits=4) == paq.PAQ_ERR_WORKSPACE
     assert _call_decode(_desc(1, 1), [0, 1], [100], splits=4, ws=FAKE, ws_bytes=64) == \

@@ -39,7 +39,7 @@ def _run(w, splits=None):
 
 @pytest.mark.parametrize("fmt,qdt,D,mode",
                          list(itertools.product(FORMATS, QDT, HEADS, MODES)))
-@pytest.mark.parametrize("splits", [1, 5])
+@pytest.mark.parametrize("splits", [1, 5, -7])
 def test_decode_formats(fmt, qdt, D, mode, splits):
     name = "dec_%s_%s_d%d_%s_s%d" % (fmt, qdt, D, mode, splits)
     print("case", name, flush=True)
@@ -47,7 +47,8 @@ def test_decode_formats(fmt, qdt, D, mode, splits):
     # and a longer ragged one
     past = np.array([0, 15, 16, 200, 90, 47])
     qlen = np.array([1, 1, 1, 1, 0, 1])
-    seed = 11 + 7 * FORMATS.index(fmt) + 3 * QDT.index(qdt) + D + MODES.index(mode)
+    seed = 11 + 7 * FORMATS.index(fmt) + 3 * QDT.index(qdt) + D + MODES.index(mode) + \
+        (splits < 0)
     w = workloads.custom(name, seed, batch=6, num_heads=16, kv_num_heads=4, head_size=D,
                          block_size=16, past=past, q_lens=qlen, q_dtype=qdt, kv_format=fmt,
                          scale_mode=mode, num_splits=splits)

@@ -47,7 +47,7 @@ def _run(w, pattern, splits, seed=0):
     desc = desc_for(w, w.token_count)
     nbytes = paq.paged_attn_decode_sparse_workspace_size(desc, w.cum_q, w.past_lens, num,
                                                          sel.shape[1], splits)
-    ws = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device="cuda")
     out = torch.full_like(g.query, float("nan"))
     paq.paged_attn_decode_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                  g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,

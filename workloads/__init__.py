@@ -10,7 +10,8 @@ The shapes and distributions follow the five workloads of the study:
   tiny_decode   batch 3, heads 4/2, D 64, block 16, 24 blocks, fp32 Q, INT8
                 per-channel; past {37,100,0}, q_len {1,1,0}
   int8_decode   batch 32, heads 32/8, D 128, block 16, fp16 Q, INT8
-                per-channel; past U{1024..4096}, q_len 1; single pass
+                per-channel; past U{1024..4096}, q_len 1; one launch, the
+                library's automatic partition (length-balanced parts)
   int4_long     batch 4, heads 32/8, D 128 (64 packed bytes), block 32, fp16
                 Q, INT4 per-channel, past 32768, q_len 1; k_scale log-uniform
                 in [1e-3, 6e4]; 128-way split-KV
@@ -67,7 +68,7 @@ class Workload:
     new_value: torch.Tensor
     k_scale: np.ndarray          # float32 (Hkv, D) or (Hkv,)
     v_scale: np.ndarray
-    num_splits: int = 1          # 0 auto, 1 single pass, >1 split-KV chunks
+    num_splits: int = 1          # 0 auto, 1 single pass, >1 split-KV chunks, -K balanced
     kind: str = "decode"         # "decode" | "prefill"
     seed: int = 0
     notes: dict = field(default_factory=dict)
@@ -178,7 +179,7 @@ def _int8_decode(seed, small=False):
     return _finish("int8_decode" + ("_small" if small else ""), rng, seed, batch=B, H=32,
                    Hkv=8, D=128, bs=16, past=past, qlen=np.ones(B, np.int32), q_dtype="f16",
                    kv_format="int8", scale_mode="channel", kv_in_dtype="f16",
-                   num_splits=1, kind="decode")
+                   num_splits=0, kind="decode")
 
 
 def _int4_long(seed, small=False):
