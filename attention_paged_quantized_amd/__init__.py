@@ -31,7 +31,8 @@ EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_d
            "paq_plan_prefill", "paged_attn_decode_workspace_size", "paged_attn_decode",
            "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary",
            "paged_attn_decode_host", "paged_attn_decode_sparse",
-           "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded")
+           "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded",
+           "paged_attn_decode_noalloc")
 
 
 class PaqDesc(ctypes.Structure):
@@ -84,6 +85,8 @@ def lib():
                 _I32P, _I32P, ctypes.c_float]
         L.paged_attn_decode.restype = ctypes.c_int32
         L.paged_attn_decode.argtypes = attn + [ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
+        L.paged_attn_decode_noalloc.restype = ctypes.c_int32
+        L.paged_attn_decode_noalloc.argtypes = attn + [ctypes.c_int32, _VP]
         L.paged_attn_prefill.restype = ctypes.c_int32
         L.paged_attn_prefill.argtypes = attn + [_VP]
         L.paged_attn_prefill_padded.restype = ctypes.c_int32
@@ -206,6 +209,19 @@ def paged_attn_decode(desc, query, out, key_cache, value_cache, k_scale, v_scale
         ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         float(softmax_scale), int(num_splits), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_noalloc(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                              softmax_scale=0.0, num_splits=0, stream=None):
+    """paged_attn_decode with the library's own per-GPU scratch as workspace
+    (no allocation; calls on one GPU must not overlap)."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    _check(lib().paged_attn_decode_noalloc(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        float(softmax_scale), int(num_splits), _stream(stream)))
 
 
 def paged_attn_prefill(desc, query, out, key_cache, value_cache, k_scale, v_scale, block_table,

@@ -21,6 +21,7 @@
 
 #include "../../include/paq.h"
 #include "decode_host.hpp"
+#include "entry.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -462,6 +463,36 @@ size_t sparse_head_bytes(int batch, int max_sel) {
 
 }  // namespace
 
+namespace paq {
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int decode_entry(const paq_desc* d, const void* query, void* out, const void* key_cache,
+                 const void* value_cache, const float* k_scale, const float* v_scale,
+                 const int32_t* block_table, const int32_t* cum_q, const int32_t* past_lens,
+                 const int32_t* cum_q_host, const int32_t* past_lens_host, float softmax_scale,
+                 int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  paq_plan p;
+  int rc = plan_decode(d, cum_q_host, past_lens_host, num_splits, 0, &p);
+  if (rc) return rc;
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  if (p.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+      return fail(PAQ_ERR_WORKSPACE, "split decode needs %llu workspace bytes, got %llu",
+                  (unsigned long long)p.workspace_bytes, (unsigned long long)workspace_bytes);
+    if (((uintptr_t)workspace) % 16)
+      return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, softmax_scale, p);
+  return run_decode(d, p, a, workspace, (hipStream_t)stream);
+}
+
+}  // namespace paq
+
 extern "C" {
 
 int32_t paq_abi_version(void) { return PAQ_ABI_VERSION; }
@@ -507,23 +538,9 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
                           const int32_t* past_lens_host, float softmax_scale,
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  paq_plan p;
-  int rc = plan_decode(d, cum_q_host, past_lens_host, num_splits, 0, &p);
-  if (rc) return rc;
-  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
-  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
-                           cum_q, past_lens);
-  if (rc) return rc;
-  if (p.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < p.workspace_bytes)
-      return fail(PAQ_ERR_WORKSPACE, "split decode needs %llu workspace bytes, got %llu",
-                  (unsigned long long)p.workspace_bytes, (unsigned long long)workspace_bytes);
-    if (((uintptr_t)workspace) % 16)
-      return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  }
-  paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
-                              block_table, cum_q, past_lens, softmax_scale, p);
-  return run_decode(d, p, a, workspace, (hipStream_t)stream);
+  return paq::decode_entry(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens, cum_q_host, past_lens_host, softmax_scale,
+                           num_splits, workspace, workspace_bytes, stream);
 }
 
 // ---- block-sparse decode ----

@@ -199,6 +199,26 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* paged_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace of split and
+ * length-balanced calls comes from a 16 MiB device array inside the library,
+ * one per GPU, held until the process ends; a call whose plan needs more
+ * (paq_plan_decode's workspace_bytes > 16 MiB) returns PAQ_ERR_WORKSPACE
+ * before anything is launched.  The call allocates nothing and calls no
+ * allocating routine.  Every call on a GPU uses that GPU's one array: calls
+ * that overlap on one GPU race, so order them (one stream, or events).  The
+ * array's arrival counters are zero when the library loads and every call
+ * leaves them zero.  Otherwise identical to paged_attn_decode (same kernels,
+ * same results). */
+int32_t paged_attn_decode_noalloc(const paq_desc* d, const void* query, void* out,
+                                  const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_table, const int32_t* cum_q,
+                                  const int32_t* past_lens, const int32_t* cum_q_host,
+                                  const int32_t* past_lens_host, float softmax_scale,
+                                  int32_t num_splits, void* stream);
+
 /* Ragged causal prefill: any q_len_b >= 0.  The grid is sized from the exact
  * max_query_len of the host cum_q; if it is 0 nothing is launched. */
 int32_t paged_attn_prefill(const paq_desc* d, const void* query, void* out,

@@ -310,3 +310,18 @@ def test_sparse_decode_checks():
     rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, 1, FAKE, 16, None)
     assert rc == paq.PAQ_ERR_WORKSPACE
+
+
+def test_noalloc_decode_refuses_plans_beyond_its_scratch():
+    """The allocation-free decode holds 16 MiB of scratch per GPU: a plan that
+    needs more is refused before anything is launched (no GPU involved)."""
+    L = paq.lib()
+    d = _desc(64, 64, mb=300, nb=20000, q="f32")      # fp32 kernel: partials per chunk
+    cum, past = _cum([1] * 64), [4000] * 64
+    need = paq.paged_attn_decode_workspace_size(d, cum, past, 64)
+    assert need > 16 << 20
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    rc = L.paged_attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, pa, pb, 0.0, 64, None)
+    assert rc == paq.PAQ_ERR_WORKSPACE and "allocation-free" in paq.paq_last_error()
