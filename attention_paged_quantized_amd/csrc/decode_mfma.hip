@@ -741,10 +741,12 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     __syncthreads();
     if (!sm_last) return;
     // Merge: every thread takes two output elements and runs a merge over
-    // the pieces by their raw maxima, 16 pieces at a time with all their loads
+    // the pieces by their raw maxima, U pieces at a time with all their loads
     // (maximum, sum and the two outputs) issued together, so the merge costs
-    // one memory round trip per 16 pieces.
-    constexpr int NT = NW * 64, U = 16;
+    // one memory round trip per U pieces.
+    // (8 pieces per round where the merge sits inside the stream partition's
+    // piece loop with two heads per wave: 16 would not fit the registers)
+    constexpr int NT = NW * 64, U = (MODE == DEC_STREAM && HW > 1) ? 8 : 16;
     for (int t0 = threadIdx.x; t0 < HW * G * D; t0 += 2 * NT) {
       int pr[2], dd[2];
       bool on[2];
@@ -850,18 +852,19 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
       const int n = (int)min((long long)(tiles - t), g1 - g);
       const long long seg = seq_first + (long long)hg * tiles;   // the segment's first tile
       const int kv_len = past + 1;
-      int nparts = 1, slot = 0, wfirst = 0;
+      int nparts = 1, slot = 0, wfirst = 0, before = 0;
       if (!(t == 0 && n == tiles)) {
         wfirst = stream_owner(seg, T, N);
         nparts = stream_owner(seg + tiles - 1, T, N) - wfirst + 1;
         slot = 2 * w + (first ? 0 : 1);
+        // only the first owner can start before the segment
+        before = (long long)wfirst * T / N < seg ? 1 : 0;
       }
       run_piece(b, hg, 32 * t, min(kv_len, 32 * (t + n)), q0, past,
                 typename WC::Blocks{-1, -1}, 0, 0, nparts, slot, [&](int p) {
                   // a piece is its workgroup's first unless that workgroup
                   // started before the segment (then it is its last)
-                  const int wp = wfirst + p;
-                  return 2 * wp + ((long long)wp * T / N < seg ? 1 : 0);
+                  return 2 * (wfirst + p) + (p == 0 ? before : 0);
                 });
       g += n;
       if (g >= g1) break;
@@ -916,7 +919,6 @@ static int launch_nw(const AttnArgs& a, hipStream_t st) {
 template <int D, int KVF, int SM, typename TQ, int HW>
 static int launch_hw_q(const AttnArgs& a, hipStream_t st) {
   if (a.dec_waves == 8) return launch_nw<D, KVF, SM, TQ, HW, 8>(a, st);
-  if (a.dec_waves == 4) return launch_nw<D, KVF, SM, TQ, HW, 4>(a, st);
   return -1;
 }
 
@@ -927,8 +929,8 @@ static int launch_hw(const AttnArgs& a, hipStream_t st) {
   return -1;
 }
 
-// HW = 128 / C heads per wave when the kv head count allows (whole 128-byte
-// lines per copied row segment), else the largest power of two dividing it.
+// HW = min(2, 128 / C) heads per wave when the kv head count allows, else
+// the largest power of two dividing it (decode_heads_per_wave).
 template <int D, int KVF, int SM>
 static int launch_dq(const AttnArgs& a, hipStream_t st) {
   constexpr int C = KvGeom<KVF, D>::C;
@@ -938,7 +940,6 @@ static int launch_dq(const AttnArgs& a, hipStream_t st) {
   switch (hw) {
     case 1: return launch_hw<D, KVF, SM, 1>(a, st);
     case 2: if constexpr (C <= 64) return launch_hw<D, KVF, SM, 2>(a, st); break;
-    case 4: if constexpr (C <= 32) return launch_hw<D, KVF, SM, 4>(a, st); break;
   }
   return -1;
 }

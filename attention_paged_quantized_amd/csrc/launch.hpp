@@ -68,11 +68,13 @@ struct AttnArgs {
 
 // Launch geometry shared by the host planner and the launchers.
 // Decode (MFMA): one wave serves this many adjacent kv heads -- 128 / row
-// bytes when the kv head count allows, else the largest power of two that
-// divides it (row bytes: head_size, or head_size / 2 for INT4).
+// bytes (whole 128-byte lines per copied row segment), at most 2 (four heads
+// per wave need more registers than a wave has: the 32-byte rows of INT4 at
+// head size 64 are copied as 64-byte segments), and only as many as divide
+// the kv head count (row bytes: head_size, or head_size / 2 for INT4).
 inline int decode_heads_per_wave(int kv_format, int head_size, int hkv) {
   const int row = (kv_format == 1 /* INT4 */) ? head_size / 2 : head_size;
-  int hw = row >= 128 ? 1 : 128 / row;
+  int hw = row >= 128 ? 1 : (128 / row > 2 ? 2 : 128 / row);
   while (hw > 1 && hkv % hw) hw /= 2;
   return hw;
 }

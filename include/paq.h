@@ -21,8 +21,10 @@
  *   value_cache  (num_blocks, block_size, kv_num_heads, cache_head_size) bytes,
  *                cache_head_size = (head_size+1)/2 for INT4, head_size otherwise
  *   block_table  int32 (batch, max_blocks_per_seq): physical block of each
- *                logical block of each sequence (unused entries may hold any
- *                value; they are never read)
+ *                logical block of each sequence.  Unused entries may hold any
+ *                value: the decode may read the entries of the batch's
+ *                longest length before a sequence's own length is known, but
+ *                never uses an entry past a sequence's blocks
  *   cum_q        int32 (batch+1): rows cum_q[b]..cum_q[b+1]-1 of query/out
  *                belong to sequence b; q_len_b = cum_q[b+1]-cum_q[b] >= 0
  *   past_lens    int32 (batch): tokens of sequence b cached before this step
@@ -44,19 +46,21 @@
  * valid until the work queued on `stream` has finished.  `stream` is a
  * hipStream_t (NULL = the default stream).  The library never allocates or
  * frees device memory, never synchronizes the stream and keeps no state
- * between calls other than its loaded kernels.
+ * between calls other than its loaded kernels (and the per-GPU workspace
+ * array of paged_attn_decode_noalloc, with its address per device).
  *
  * Errors.  Every check runs on the host before anything is launched: a
  * non-zero status means nothing was launched and nothing written.
  * paq_last_error() describes the most recent failure of the calling thread.
  * Preconditions that are NOT checked (device-resident data): block ids in
  * [0, num_blocks), device cum_q/past_lens equal to their host copies, finite
- * positive scales, finite inputs.  Key scales may lie far outside the 16-bit
- * ranges (tested over [2^-60, 2^100] per channel): the 16-bit kernels fold
- * k_scale / M into the query with M the power of two >= the kv head's largest
- * key scale, and keep softmax_scale * M in fp32; the products
- * softmax_scale * k_scale * |q . k codes| must stay below ~2^120.  Value
- * scales must keep the outputs inside the query dtype's range.
+ * positive scales, finite inputs.  Key scales may be any finite positive
+ * fp32 value, FLT_MAX and subnormals included, per channel or per head: the
+ * kernels keep the softmax in raw score units with fp32 running maxima, fold
+ * k_scale / M into the query (M a power of two near the kv head's largest key
+ * scale) and clamp the score factor softmax_scale * M to the finite fp32
+ * range, so no intermediate overflows.  Value scales must keep the outputs
+ * inside the query dtype's range.
  */
 #ifndef PAQ_H
 #define PAQ_H
@@ -81,11 +85,13 @@ enum paq_status {
 enum paq_dtype { PAQ_DT_F32 = 0, PAQ_DT_F16 = 1, PAQ_DT_BF16 = 2 };
 
 /* KV storage formats.
- * INT8: two's-complement byte, codes in [-127, 127].
+ * INT8: two's-complement byte, codes in [-127, 127] ("INT8-KV Tensor-Core
+ *       DynamicSparseAttention", section 1: INT8 KV cache).
  * INT4: two 4-bit two's-complement codes in [-7, 7] per byte ("ONNX Runtime:
  *       INT4 Paged KV Cache", section 2); channel 2j in the low nibble,
  *       channel 2j+1 in the high nibble.
- * FP8_E4M3: OCP E4M3 (bias 7, max 448, S.1111.111 NaN, no infinities). */
+ * FP8_E4M3: an FP8 KV cache ("FlashInfer FP8 KV-cache prefill", section 1),
+ *       stored as OCP E4M3 (bias 7, max 448, S.1111.111 NaN, no infinities). */
 enum paq_kv_format { PAQ_KV_INT8 = 0, PAQ_KV_INT4 = 1, PAQ_KV_FP8_E4M3 = 2 };
 
 enum paq_scale_mode { PAQ_SCALE_PER_CHANNEL = 0, PAQ_SCALE_PER_HEAD = 1 };
@@ -247,7 +253,12 @@ int32_t paged_attn_prefill_padded(const paq_desc* d, const void* query, void* ou
                                   const int32_t* past_lens_host, float softmax_scale,
                                   int32_t max_query_len, void* stream);
 
-/* Quantize rows cum_q[b]..cum_q[b+1]-1 of key/value (token_count, kv_num_heads,
+/* The quantized cache write the pages' kernels read from: the INT4 cache of
+ * "ONNX Runtime: INT4 Paged KV Cache" (sections 2-3: symmetric codes with
+ * fp32 per-channel scales, two codes per byte), the INT8 cache of
+ * "INT8-KV Tensor-Core DynamicSparseAttention" (section 1) and the FP8 cache
+ * of "FlashInfer FP8 KV-cache prefill" (section 1).
+ * Quantize rows cum_q[b]..cum_q[b+1]-1 of key/value (token_count, kv_num_heads,
  * head_size; dtype kv_in_dtype) and store row i of sequence b at position
  * past_b + i.  code = clamp(round_half_even(fl32(x / s))) with +-127 (INT8),
  * +-7 (INT4), or E4M3 round-half-even saturating to +-448 (FP8); x / s is the
