@@ -32,7 +32,8 @@ EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_d
            "paged_attn_prefill", "kv_quant_append", "kv_quant_append_rotary",
            "paged_attn_decode_host", "paged_attn_decode_sparse",
            "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded",
-           "paged_attn_decode_noalloc")
+           "paged_attn_decode_noalloc", "paged_attn_prefill_sparse",
+           "paged_attn_prefill_sparse_workspace_size")
 
 
 class PaqDesc(ctypes.Structure):
@@ -102,6 +103,13 @@ def lib():
         L.paged_attn_decode_sparse_workspace_size.argtypes = [ctypes.POINTER(PaqDesc), _I32P,
                                                               _I32P, _I32P, ctypes.c_int32,
                                                               ctypes.c_int32]
+        L.paged_attn_prefill_sparse.restype = ctypes.c_int32
+        L.paged_attn_prefill_sparse.argtypes = attn[:-1] + [_VP, _VP, _I32P, ctypes.c_int32,
+                                                            ctypes.c_float, _VP, ctypes.c_size_t,
+                                                            _VP]
+        L.paged_attn_prefill_sparse_workspace_size.restype = ctypes.c_size_t
+        L.paged_attn_prefill_sparse_workspace_size.argtypes = [ctypes.POINTER(PaqDesc), _I32P,
+                                                               _I32P, _I32P, ctypes.c_int32]
         L.paged_attn_decode_host.restype = ctypes.c_int32
         L.paged_attn_decode_host.argtypes = [ctypes.POINTER(PaqDesc), _VP, _VP, _VP, _VP, _VP,
                                              _VP, _VP, _VP, _VP, ctypes.c_float,
@@ -323,3 +331,31 @@ def paged_attn_decode_sparse(desc, query, out, key_cache, value_cache, k_scale, 
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         _dev(sel_blocks), _dev(num_sel), pc, int(sel_blocks.shape[1]), float(softmax_scale),
         int(num_splits), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_prefill_sparse_workspace_size(desc, cum_q_host, past_lens_host, num_sel_host,
+                                             max_sel):
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    c, pc = _host_i32(num_sel_host)
+    return int(lib().paged_attn_prefill_sparse_workspace_size(ctypes.byref(desc), pa, pb, pc,
+                                                              int(max_sel)))
+
+
+def paged_attn_prefill_sparse(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                              sel_blocks, num_sel, num_sel_host, softmax_scale=0.0,
+                              workspace=None, stream=None):
+    """Block-sparse prefill: sel_blocks (batch, max_sel) and num_sel (batch) are
+    int32 device tensors (None, None with max_sel 0: local blocks only);
+    num_sel_host their host copy."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    c, pc = _host_i32(num_sel_host)
+    max_sel = 0 if sel_blocks is None else int(sel_blocks.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attn_prefill_sparse(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        _dev(sel_blocks), _dev(num_sel), pc, max_sel, float(softmax_scale), _dev(workspace),
+        ws_bytes, _stream(stream)))

@@ -128,6 +128,13 @@ int launch_sparse_compact(const int32_t* block_table, int max_blocks, const int3
                           const int32_t* num_sel, int max_sel, const int32_t* cum_q,
                           const int32_t* past_lens, int block_size, int batch, int32_t* compact,
                           int32_t* eff_past, hipStream_t st);
+// block-sparse prefill: selected earlier blocks + the blocks holding new
+// tokens -> compact table (row stride `stride`) + effective past
+int launch_sparse_prefill_compact(const int32_t* block_table, int max_blocks, const int32_t* sel,
+                                  const int32_t* num_sel, int max_sel, const int32_t* cum_q,
+                                  const int32_t* past_lens, int block_size, int batch,
+                                  int stride, int32_t* compact, int32_t* eff_past,
+                                  hipStream_t st);
 
 // Shape support of the MFMA kernels (host checks before choosing a path).
 bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype);

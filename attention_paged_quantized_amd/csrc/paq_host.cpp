@@ -461,6 +461,40 @@ size_t sparse_head_bytes(int batch, int max_sel) {
   return align_up((size_t)batch * max_sel * 4) + align_up((size_t)batch * 4);
 }
 
+// Block-sparse prefill plan: the dense prefill over the compact table of the
+// selected earlier blocks followed by the blocks holding new tokens, whose
+// chunk starts at num_sel * block_size + past % block_size.  *stride gets the
+// compact table's row length (max_sel + the most local blocks of a sequence).
+int plan_sparse_prefill(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
+                        const int32_t* num_sel_host, int max_sel, paq_desc* dc,
+                        std::vector<int32_t>* past_c, int* stride, paq_plan* p) {
+  SeqStats st;
+  int rc = validate(d, cum_q_host, past_host, &st);
+  if (rc) return rc;
+  if (max_sel < 0) return fail(PAQ_ERR_INVALID_ARG, "max_sel %d < 0", max_sel);
+  if (d->batch > 0 && max_sel > 0 && !num_sel_host)
+    return fail(PAQ_ERR_INVALID_ARG, "num_sel_host is NULL");
+  int max_local = 0;
+  past_c->assign(d->batch, 0);
+  for (int b = 0; b < d->batch; ++b) {
+    const int q = cum_q_host[b + 1] - cum_q_host[b];
+    if (q == 0) continue;
+    const int past = past_host[b], bs = d->block_size;
+    const int n = max_sel > 0 ? num_sel_host[b] : 0;
+    if (n < 0 || n > max_sel || n > past / bs)
+      return fail(PAQ_ERR_INVALID_ARG,
+                  "sequence %d selects %d blocks (needs 0..min(max_sel %d, its %d blocks "
+                  "before the first new token))", b, n, max_sel, past / bs);
+    const int local = (int)(((long)past + q + bs - 1) / bs) - past / bs;
+    max_local = std::max(max_local, local);
+    (*past_c)[b] = n * bs + past % bs;
+  }
+  *dc = *d;
+  *stride = max_sel + max_local;
+  dc->max_blocks_per_seq = *stride;
+  return plan_prefill(dc, cum_q_host, past_c->data(), p);
+}
+
 }  // namespace
 
 namespace paq {
@@ -668,6 +702,62 @@ int32_t paged_attn_prefill_padded(const paq_desc* d, const void* query, void* ou
   if (max_query_len < 1) return fail(PAQ_ERR_INVALID_ARG, "max_query_len %d < 1", max_query_len);
   return run_prefill(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
                      past_lens, cum_q_host, past_lens_host, softmax_scale, max_query_len, stream);
+}
+
+// ---- block-sparse prefill ----
+
+int32_t paged_attn_prefill_sparse(const paq_desc* d, const void* query, void* out,
+                                  const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_table, const int32_t* cum_q,
+                                  const int32_t* past_lens, const int32_t* cum_q_host,
+                                  const int32_t* past_lens_host, const int32_t* sel_blocks,
+                                  const int32_t* num_sel, const int32_t* num_sel_host,
+                                  int32_t max_sel, float softmax_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  paq_desc dc;
+  std::vector<int32_t> past_c;
+  paq_plan p;
+  int stride = 0;
+  int rc = plan_sparse_prefill(d, cum_q_host, past_lens_host, num_sel_host, max_sel, &dc,
+                               &past_c, &stride, &p);
+  if (rc) return rc;
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  if (max_sel > 0 && (!sel_blocks || !num_sel))
+    return fail(PAQ_ERR_INVALID_ARG, "sel_blocks / num_sel is NULL");
+  const size_t need = sparse_head_bytes(d->batch, stride);
+  if (!workspace || workspace_bytes < need)
+    return fail(PAQ_ERR_WORKSPACE, "sparse prefill needs %llu workspace bytes, got %llu",
+                (unsigned long long)need, (unsigned long long)workspace_bytes);
+  if (((uintptr_t)workspace) % 16)
+    return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int32_t* compact = (int32_t*)workspace;
+  int32_t* eff_past = (int32_t*)((char*)workspace + align_up((size_t)d->batch * stride * 4));
+  rc = launched(paq::launch_sparse_prefill_compact(block_table, d->max_blocks_per_seq,
+                                                   sel_blocks, num_sel, max_sel, cum_q,
+                                                   past_lens, d->block_size, d->batch, stride,
+                                                   compact, eff_past, (hipStream_t)stream),
+                "sparse prefill block selection");
+  if (rc) return rc;
+  return run_prefill(&dc, query, out, key_cache, value_cache, k_scale, v_scale, compact, cum_q,
+                     eff_past, cum_q_host, past_c.data(), softmax_scale, 0, stream);
+}
+
+size_t paged_attn_prefill_sparse_workspace_size(const paq_desc* d, const int32_t* cum_q_host,
+                                                const int32_t* past_lens_host,
+                                                const int32_t* num_sel_host, int32_t max_sel) {
+  paq_desc dc;
+  std::vector<int32_t> past_c;
+  paq_plan p;
+  int stride = 0;
+  if (plan_sparse_prefill(d, cum_q_host, past_lens_host, num_sel_host, max_sel, &dc, &past_c,
+                          &stride, &p))
+    return 0;
+  if (p.path == PAQ_PATH_NONE) return 0;
+  return sparse_head_bytes(d->batch, stride);
 }
 
 int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,

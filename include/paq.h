@@ -1,7 +1,7 @@
 /*
  * paq.h -- C ABI of the MI355X (gfx950) paged, quantized-KV attention library.
  *
- * Three operations over a block-paged KV cache stored as INT8, packed INT4 or
+ * Operations over a block-paged KV cache stored as INT8, packed INT4 or
  * FP8 E4M3 with fp32 scales:
  *   kv_quant_append     quantize a step's new key/value rows into their slots
  *                       (kv_quant_append_rotary: rotary embedding first);
@@ -9,9 +9,11 @@
  *                       split-KV ("flash decoding") with a log-sum-exp merge;
  *   paged_attn_prefill  ragged, causal, chunked prefill;
  *   paged_attn_decode_sparse  decode over caller-selected KV blocks;
+ *   paged_attn_prefill_sparse prefill over caller-selected earlier blocks
+ *                             plus the blocks holding the new tokens;
  *   paged_attn_decode_host  the same decode on the host CPU, host-resident data.
  *
- * Problem statement (shared by all three; the cache shape with
+ * Problem statement (shared by all of them; the cache shape with
  * cache_head_size is from "ONNX Runtime: INT4 Paged KV Cache", section 2; the
  * cumulative query lengths and their host copy are from "PagedAttention FA
  * path: exact max_query_len", section 1):
@@ -303,6 +305,44 @@ size_t paged_attn_decode_sparse_workspace_size(const paq_desc* d, const int32_t*
                                                const int32_t* past_lens_host,
                                                const int32_t* num_sel_host, int32_t max_sel,
                                                int32_t num_splits);
+
+/* Block-sparse prefill ("INT8-KV Tensor-Core DynamicSparseAttention",
+ * section 1, which names prefill beside decode; the page gives no selection
+ * rule, so the selection is an input).  The q_len_b new rows of sequence b
+ * attend causally, as in paged_attn_prefill, to the keys of
+ *   - every block that holds one of its new tokens (logical blocks
+ *     past_b / block_size .. (kv_len_b - 1) / block_size, including the
+ *     cached keys that share the first of them), and
+ *   - the earlier blocks sel_blocks[b][0 .. num_sel[b]).
+ *   sel_blocks   int32 (batch, max_sel), device: ascending logical block
+ *                indices, each < past_b / block_size (blocks holding cached
+ *                keys only; not checked: device data, like block ids)
+ *   num_sel      int32 (batch), device; num_sel_host its host copy, each in
+ *                [0, min(max_sel, past_b / block_size)] for sequences with
+ *                new rows (checked on the host).  max_sel may be 0 (local
+ *                blocks only; sel_blocks and num_sel may then be NULL).
+ * Runs a small kernel that writes a compact block table (the selected
+ * blocks, then the local ones) and effective past lengths
+ * num_sel * block_size + past % block_size into `workspace`, then the dense
+ * prefill kernels over it (the causal rule carries over: every selected key
+ * precedes the first new token).  `workspace` (device, 16-byte aligned) must
+ * hold paged_attn_prefill_sparse_workspace_size() bytes; it is overwritten.
+ * Otherwise as paged_attn_prefill. */
+int32_t paged_attn_prefill_sparse(const paq_desc* d, const void* query, void* out,
+                                  const void* key_cache, const void* value_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_table, const int32_t* cum_q,
+                                  const int32_t* past_lens, const int32_t* cum_q_host,
+                                  const int32_t* past_lens_host, const int32_t* sel_blocks,
+                                  const int32_t* num_sel, const int32_t* num_sel_host,
+                                  int32_t max_sel, float softmax_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of paged_attn_prefill_sparse (0 when the arguments are
+ * invalid or there is nothing to do). */
+size_t paged_attn_prefill_sparse_workspace_size(const paq_desc* d, const int32_t* cum_q_host,
+                                                const int32_t* past_lens_host,
+                                                const int32_t* num_sel_host, int32_t max_sel);
 
 /* GQA decode on the host CPU over host-resident caches: the CPU workload of
  * "GQA GEMV decode" (sections 2-3).  Every pointer is HOST memory (including

@@ -51,6 +51,10 @@ def _cum(qlens):
     return np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
 
 
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
 COUNTER_BYTES = 16384 * 4      # arrival counters at the head of every decode workspace
 
 
@@ -310,6 +314,40 @@ def test_sparse_decode_checks():
     rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, 1, FAKE, 16, None)
     assert rc == paq.PAQ_ERR_WORKSPACE
+
+
+def test_sparse_prefill_checks():
+    """Selections reach only blocks before the first new token; the workspace
+    holds the compact table (max_sel + the most local blocks per row) and the
+    effective past lengths; refusals come before any launch."""
+    L = paq.lib()
+    d = _desc(3, 25)
+    cum, past = [0, 10, 10, 25], [40, 5, 16]       # local blocks: 2..3, none, 1..1
+    # 40 // 16 = 2 earlier blocks for sequence 0, 1 for sequence 2
+    ws = paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, [2, 0, 1], 2)
+    assert ws == _align(3 * (2 + 2) * 4) + _align(3 * 4)
+    assert paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, None, 0) == \
+        _align(3 * 2 * 4) + _align(3 * 4)
+    assert paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, [3, 0, 1], 3) == 0
+    assert paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, [0, 0, 2], 2) == 0
+    assert paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, [2, 0, 1], 1) == 0
+    # sequence 1 has no new row: its count is not read
+    assert paq.paged_attn_prefill_sparse_workspace_size(d, cum, past, [2, 99, 1], 2) > 0
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    c, pc = paq._host_i32([0, 0, 2])
+    rc = L.paged_attn_prefill_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 2, 0.0, FAKE, 1 << 20,
+                                     None)
+    assert rc == paq.PAQ_ERR_INVALID_ARG and "selects 2 blocks" in paq.paq_last_error()
+    c, pc = paq._host_i32([2, 0, 1])
+    rc = L.paged_attn_prefill_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 2, 0.0, FAKE, 16, None)
+    assert rc == paq.PAQ_ERR_WORKSPACE
+    rc = L.paged_attn_prefill_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, pa, pb, None, None, pc, 2, 0.0, FAKE, 1 << 20,
+                                     None)
+    assert rc == paq.PAQ_ERR_INVALID_ARG and "sel_blocks" in paq.paq_last_error()
 
 
 def test_noalloc_decode_refuses_plans_beyond_its_scratch():

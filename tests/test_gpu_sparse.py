@@ -89,3 +89,98 @@ def test_sparse_decode_full_size_window():
     print("case sparse full", flush=True)
     w = workloads.make("int8_decode")
     _run(w, "window", 1)
+
+
+# ---- block-sparse prefill (paged_attn_prefill_sparse vs block_sparse_prefill) ----
+
+def prefill_selection(w, pattern, rng):
+    """Ascending selected earlier blocks (each below past // block_size)."""
+    nfb = w.past_lens // w.block_size
+    rows = []
+    for b in range(w.batch):
+        n = int(nfb[b])
+        if pattern == "all":
+            s = list(range(n))
+        elif pattern == "window":        # the 2 blocks before the local ones + every 3rd
+            s = sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3))))
+        else:                            # random half
+            s = sorted(rng.choice(n, n // 2, replace=False).tolist()) if n else []
+        rows.append(s)
+    m = max(1, max(len(r) for r in rows))
+    sel = np.zeros((w.batch, m), np.int32)
+    num = np.array([len(r) for r in rows], np.int32)
+    for b, r in enumerate(rows):
+        sel[b, :len(r)] = r
+    return sel, num
+
+
+def _run_prefill(w, pattern, seed=0, seqs=None):
+    rng = np.random.default_rng(seed)
+    if pattern == "none":
+        sel, num = None, np.zeros(w.batch, np.int32)
+    else:
+        sel, num = prefill_selection(w, pattern, rng)
+    max_sel = 0 if sel is None else sel.shape[1]
+    g = Device(w).fill()
+    desc = desc_for(w, w.token_count)
+    nbytes = paq.paged_attn_prefill_sparse_workspace_size(desc, w.cum_q, w.past_lens, num,
+                                                          max_sel)
+    ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device="cuda")
+    out = torch.full_like(g.query, float("nan"))
+    dsel = None if sel is None else torch.from_numpy(sel).cuda()
+    dnum = None if sel is None else torch.from_numpy(num).cuda()
+    paq.paged_attn_prefill_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                  g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, dsel,
+                                  dnum, num, 0.0, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    kc, vc = oracle_caches(w)
+    osel = np.zeros((w.batch, 1), np.int32) if sel is None else sel
+    seqs = range(w.batch) if seqs is None else seqs
+    # the oracle per sequence (sequences are independent): the sampled ones
+    rows = np.concatenate([np.arange(w.cum_q[b], w.cum_q[b + 1]) for b in seqs]).astype(int)
+    qlen = np.array([w.cum_q[b + 1] - w.cum_q[b] for b in seqs])
+    cum = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    ref = sparse.block_sparse_prefill(f32(w.query)[rows], kc, vc, w.k_scale, w.v_scale,
+                                      w.block_table[list(seqs)], cum, w.past_lens[list(seqs)],
+                                      w.kv_format, osel[list(seqs)], num[list(seqs)])
+    compare.check(got[rows], ref, w.q_dtype, w.name)
+    if len(rows) == got.shape[0]:
+        return
+    assert np.all(np.isfinite(got)), "non-finite rows outside the sample"
+
+
+def _wp(fmt, qdt, D, seed):
+    return workloads.custom("sparse_prefill", seed, batch=6, num_heads=32, kv_num_heads=8,
+                            head_size=D, block_size=16,
+                            past=np.array([70, 0, 48, 20, 37, 300]),
+                            q_lens=np.array([9, 5, 40, 0, 70, 33]), q_dtype=qdt,
+                            kv_format=fmt, kind="prefill",
+                            scale_mode="head" if fmt == "fp8" else "channel")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4", "fp8"])
+@pytest.mark.parametrize("qdt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("pattern", ["window", "random", "none"])
+def test_sparse_prefill(fmt, qdt, pattern):
+    print("case sparse prefill", fmt, qdt, pattern, flush=True)
+    _run_prefill(_wp(fmt, qdt, 128, 31), pattern, seed=5)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_sparse_prefill_head64_and_all_blocks(fmt):
+    print("case sparse prefill D64 all", fmt, flush=True)
+    _run_prefill(_wp(fmt, "f16", 64, 37), "all")
+
+
+def test_sparse_prefill_full_size_window():
+    """int8_prefill shape (64 ragged sequences, pasts up to 2048) with the
+    window + strided selection; the oracle on 6 sequences, every row and
+    head, the longest included."""
+    print("case sparse prefill full", flush=True)
+    w = workloads.make("int8_prefill")
+    qlen = np.diff(w.cum_q)
+    order = np.argsort(-(qlen * 4096 + w.past_lens))
+    seqs = sorted(set(order[:3].tolist()) | set(np.random.default_rng(3).choice(
+        w.batch, 3, replace=False).tolist()))
+    _run_prefill(w, "window", seqs=seqs)
