@@ -33,7 +33,7 @@ EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_d
            "paged_attn_decode_host", "paged_attn_decode_sparse",
            "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded",
            "paged_attn_decode_noalloc", "paged_attn_prefill_sparse",
-           "paged_attn_prefill_sparse_workspace_size")
+           "paged_attn_prefill_sparse_workspace_size", "paged_attn_prefill_k_per_use")
 
 
 class PaqDesc(ctypes.Structure):
@@ -90,6 +90,8 @@ def lib():
         L.paged_attn_decode_noalloc.argtypes = attn + [ctypes.c_int32, _VP]
         L.paged_attn_prefill.restype = ctypes.c_int32
         L.paged_attn_prefill.argtypes = attn + [_VP]
+        L.paged_attn_prefill_k_per_use.restype = ctypes.c_int32
+        L.paged_attn_prefill_k_per_use.argtypes = attn + [_VP]
         L.paged_attn_prefill_padded.restype = ctypes.c_int32
         L.paged_attn_prefill_padded.argtypes = attn + [ctypes.c_int32, _VP]
         L.kv_quant_append.restype = ctypes.c_int32
@@ -254,6 +256,19 @@ def paged_attn_prefill_padded(desc, query, out, key_cache, value_cache, k_scale,
         ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         float(softmax_scale), int(max_query_len), _stream(stream)))
+
+
+def paged_attn_prefill_k_per_use(desc, query, out, key_cache, value_cache, k_scale, v_scale,
+                                 block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                                 softmax_scale=0.0, stream=None):
+    """paged_attn_prefill with K codes kept raw in LDS and converted by every
+    wave at each use (the staging scheme the default is compared with)."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    _check(lib().paged_attn_prefill_k_per_use(
+        ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
+        _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
+        float(softmax_scale), _stream(stream)))
 
 
 def kv_quant_append(desc, kv_in_dtype, key, value, key_cache, value_cache, k_scale, v_scale,

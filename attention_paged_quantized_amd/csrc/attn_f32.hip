@@ -10,8 +10,9 @@
 // output ("GQA GEMV decode", section 2: flash decoding partials).
 //
 // Keys are processed 256 at a time, one per thread for the scores (online
-// softmax across chunks), then every thread owns one channel of one key slice
-// for the probability-weighted value sum.  Scores stay in raw units (query
+// softmax across chunks; the thread loads its key's key and value rows at
+// once and leaves the value row in LDS), then every thread owns one channel of
+// one key slice for the probability-weighted value sum over those LDS rows.  Scores stay in raw units (query
 // times key scale over its power-of-two normaliser, dotted with the codes);
 // exponents are formed as (raw - raw max) * factor, so key scales anywhere in
 // the finite fp32 range neither overflow nor produce a NaN.
@@ -24,20 +25,26 @@ constexpr int kF32Threads = 256;
 constexpr int kF32MaxGroup = kF32KernelMaxGroup;
 constexpr int kF32MaxD = 128;
 
+constexpr int kF32Units = kF32MaxD / 16;      // 16-byte units of the longest row
+
+// 16 channel values from channel d0 (a multiple of 16) of a cache row held as
+// its raw 16-byte units (the index is a compile-time constant wherever the
+// callers' loops are unrolled).
 template <int KVF>
-__device__ __forceinline__ void load_codes16(const uint8_t* row, int d0, float (&k)[16]) {
+__device__ __forceinline__ void codes16(const u32x4 (&w)[kF32Units], int d0, float (&k)[16]) {
   if constexpr (KVF == KV_INT4) {
-    u32x2 w = *reinterpret_cast<const u32x2*>(row + d0 / 2);
+    const u32x4 u = w[d0 / 32];                 // bytes d0/2 .. d0/2 + 7
+    const uint32_t x0 = (d0 & 16) ? u[2] : u[0], x1 = (d0 & 16) ? u[3] : u[1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      uint32_t nib = (w[i / 8] >> (4 * (i % 8))) & 0xF;
+      const uint32_t nib = ((i < 8 ? x0 : x1) >> (4 * (i % 8))) & 0xF;
       k[i] = (float)((int)(nib ^ 8u) - 8);
     }
   } else {
-    u32x4 w = *reinterpret_cast<const u32x4*>(row + d0);
+    const u32x4 u = w[d0 / 16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      uint32_t byte = (w[i / 4] >> (8 * (i % 4))) & 0xFF;
+      const uint32_t byte = (u[i / 4] >> (8 * (i % 4))) & 0xFF;
       if constexpr (KVF == KV_INT8) {
         k[i] = (float)(int8_t)byte;
       } else {
@@ -47,10 +54,11 @@ __device__ __forceinline__ void load_codes16(const uint8_t* row, int d0, float (
   }
 }
 
+// the value of channel d of a cache row in LDS
 template <int KVF>
-__device__ __forceinline__ float load_code1(const uint8_t* row, int d) {
+__device__ __forceinline__ float code_at(const uint8_t* row, int d) {
   if constexpr (KVF == KV_INT4) {
-    uint32_t nib = (row[d / 2] >> (4 * (d & 1))) & 0xF;
+    const uint32_t nib = (row[d / 2] >> (4 * (d & 1))) & 0xF;
     return (float)((int)(nib ^ 8u) - 8);
   } else if constexpr (KVF == KV_INT8) {
     return (float)(int8_t)row[d];
@@ -69,13 +77,37 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int C = (KVF == KV_INT4) ? D / 2 : D;
   const int tid = threadIdx.x;
 
-  // sequence of this row: the largest b with cum_q[b] <= r
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.cum_q[mid] <= r) lo = mid; else hi = mid;
+  // Loads that do not depend on the row's sequence go first, so that they
+  // share one memory latency with the sequence search: this thread's key
+  // scale (for the normaliser) and its query elements with their scales.
+  const float ks_mine = (SM == SCALE_CHANNEL) ? (tid < D ? fabsf(a.k_scale[g * D + tid]) : 0.f)
+                                              : fabsf(a.k_scale[g]);
+  constexpr int kQPer = kF32MaxGroup * kF32MaxD / kF32Threads;
+  const TQ* q = reinterpret_cast<const TQ*>(a.query);
+  float qv[kQPer], sv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = tid + u * kF32Threads;
+    qv[u] = 0.f;
+    sv[u] = 0.f;
+    if (i < G * D) {
+      const int hh = i / D, d = i % D;
+      qv[u] = to_f32(q[((size_t)r * H + g * G + hh) * D + d]);
+      sv[u] = (SM == SCALE_CHANNEL) ? a.k_scale[g * D + d] : a.k_scale[g];
+    }
   }
-  const int b = lo;
+
+  // sequence of this row: the largest b with cum_q[b] <= r, i.e. the number
+  // of entries cum_q[1..batch] that are <= r (cum_q never decreases), counted
+  // by every wave 64 entries per round trip
+  const int wave = tid / 64, lane = tid % 64;
+  int b = 0;
+  for (int base = 1; base <= a.batch; base += 64) {
+    const int idx = base + lane;
+    const unsigned long long le = __ballot(idx <= a.batch && a.cum_q[idx] <= r);
+    b += __builtin_popcountll(le);
+    if (le != ~0ull) break;
+  }
   const int i = r - a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - a.cum_q[b];
   const int past = a.past_lens[b];
@@ -91,17 +123,17 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   __shared__ float sc[kF32MaxGroup][kF32Threads];
   __shared__ float m_sh[kF32MaxGroup], l_sh[kF32MaxGroup], alpha_sh[kF32MaxGroup];
   __shared__ int e_sh;
+  __shared__ __attribute__((aligned(16))) uint8_t vrows[kF32Threads * (kF32MaxD + 16)];
 
   // q' = q * s / M with M = 2^e >= max|s| of this kv head (exact scaling; M
   // finite for every finite scale): raw scores q'.codes never overflow, and
   // the score factor c2 = softmax_scale * M * log2(e) is kept finite
-  const int e = key_scale_exponent<SM>(a.k_scale, g, D, &e_sh);
+  const int e = key_scale_exponent_of<SM>(ks_mine, &e_sh);
   const float c2 = score_factor_log2(a.softmax_scale, e, 1.f);
-  const TQ* q = reinterpret_cast<const TQ*>(a.query);
-  for (int i = tid; i < G * D; i += kF32Threads) {
-    const int hh = i / D, d = i % D;
-    const float s = (SM == SCALE_CHANNEL) ? a.k_scale[g * D + d] : a.k_scale[g];
-    qs[hh][d] = to_f32(q[((size_t)r * H + g * G + hh) * D + d]) * ldexpf(s, -e);
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i2 = tid + u * kF32Threads;
+    if (i2 < G * D) qs[i2 / D][i2 % D] = qv[u] * ldexpf(sv[u], -e);
   }
   if (tid < G) { m_sh[tid] = -INFINITY; l_sh[tid] = 0.f; }
 
@@ -113,25 +145,40 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   for (int hh = 0; hh < kF32MaxGroup; ++hh) acc[hh] = 0.f;
   __syncthreads();
 
-  const int wave = tid / 64, lane = tid % 64;
+  const int vst = C + 16;                 // LDS value row stride (16-byte aligned, padded)
   for (int base = kbeg; base < kend; base += kF32Threads) {
-    // scores: one key per thread
+    // one key per thread: its key and value rows are loaded together (every
+    // unit in flight at once), the value row goes to LDS for the weighted sum
     const int j = base + tid;
     float dot[kF32MaxGroup];
 #pragma unroll
     for (int hh = 0; hh < kF32MaxGroup; ++hh) dot[hh] = 0.f;
     if (j < kend) {
       const int blk = table[j / bs];
-      const uint8_t* row = a.key_cache + (((size_t)blk * bs + j % bs) * hkv + g) * C;
-      for (int d0 = 0; d0 < D; d0 += 16) {
+      const size_t off = (((size_t)blk * bs + j % bs) * hkv + g) * C;
+      u32x4 kw[kF32Units], vw[kF32Units];
+#pragma unroll
+      for (int u = 0; u < kF32Units; ++u) {
+        if (16 * u >= C) break;
+        kw[u] = *reinterpret_cast<const u32x4*>(a.key_cache + off + 16 * u);
+        vw[u] = *reinterpret_cast<const u32x4*>(a.value_cache + off + 16 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < kF32Units; ++u) {
+        if (16 * u >= C) break;
+        *reinterpret_cast<u32x4*>(vrows + tid * vst + 16 * u) = vw[u];
+      }
+#pragma unroll
+      for (int u = 0; u < kF32Units; ++u) {
+        if (16 * u >= D) break;
         float k[16];
-        load_codes16<KVF>(row, d0, k);
+        codes16<KVF>(kw, 16 * u, k);
 #pragma unroll
         for (int hh = 0; hh < kF32MaxGroup; ++hh) {
           if (hh < G) {
             float s = dot[hh];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s = fmaf(qs[hh][d0 + e], k[e], s);
+            for (int e = 0; e < 16; ++e) s = fmaf(qs[hh][16 * u + e], k[e], s);
             dot[hh] = s;
           }
         }
@@ -171,11 +218,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       for (int hh = 0; hh < kF32MaxGroup; ++hh)
         if (hh < G) acc[hh] *= alpha_sh[hh];
       const int jn = min(kend - base, kF32Threads);
+#pragma unroll 4
       for (int t = my_slice; t < jn; t += nslice) {
-        const int jj = base + t;
-        const int blk = table[jj / bs];
-        const uint8_t* row = a.value_cache + (((size_t)blk * bs + jj % bs) * hkv + g) * C;
-        const float v = load_code1<KVF>(row, my_d);
+        const float v = code_at<KVF>(vrows + t * vst, my_d);
 #pragma unroll
         for (int hh = 0; hh < kF32MaxGroup; ++hh)
           if (hh < G) acc[hh] = fmaf(sc[hh][t], v, acc[hh]);

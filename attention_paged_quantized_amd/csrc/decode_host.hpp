@@ -23,8 +23,8 @@ struct HostDecodeArgs {
   int threads;
 };
 
-// Returns 0, or -1 for a shape it does not handle (more than 64 query heads
-// per kv head).
+// Returns 0, or -1 for a shape it does not handle (a head size other than
+// 64 or 128).
 int host_decode(const HostDecodeArgs& a);
 
 }  // namespace paq

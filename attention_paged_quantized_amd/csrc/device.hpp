@@ -212,6 +212,21 @@ __device__ __forceinline__ int scale_exponent(float smax) {
 // scale_exponent of kv head g's key scales, computed by a whole workgroup
 // (blockDim.x a multiple of 64, >= D; *slot is LDS scratch).  Every thread
 // returns the same value.
+// (key_scale_exponent_of: the same from the value this thread loaded -- its
+// channel's |scale| for threads below D, else 0; the per-head |scale|)
+template <int SM>
+__device__ __forceinline__ int key_scale_exponent_of(float m, int* slot) {
+  if constexpr (SM == SCALE_CHANNEL) {
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (threadIdx.x == 0) *slot = 0;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) atomicMax(slot, __float_as_int(m));
+    __syncthreads();
+    m = __int_as_float(*slot);
+  }
+  return scale_exponent(m);
+}
+
 template <int SM>
 __device__ __forceinline__ int key_scale_exponent(const float* k_scale, int g, int D, int* slot) {
   float m;

@@ -53,6 +53,7 @@ struct AttnArgs {
   int part_count;       // fp32 split-KV: partials per (row, head) in the workspace
   int grid_x;           // 1-D launch grid (MFMA decode and prefill: from the host plan)
   int pf_ntq;           // prefill: query tiles of every sequence if all have the same, else 0
+  int pf_k_per_use;     // prefill: K codes converted per use (comparison variant)
   int max_query_len;    // exact, from the host cum_q
   int max_kv_len;       // longest sequence with new rows (host)
   int block_size_log2;  // block_size is a power of two

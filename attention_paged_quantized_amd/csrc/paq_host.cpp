@@ -644,10 +644,15 @@ int run_prefill(const paq_desc* d, const void* query, void* out, const void* key
                 const void* value_cache, const float* k_scale, const float* v_scale,
                 const int32_t* block_table, const int32_t* cum_q, const int32_t* past_lens,
                 const int32_t* cum_q_host, const int32_t* past_lens_host, float softmax_scale,
-                int padded_mql, void* stream) {
+                int padded_mql, void* stream, bool k_per_use = false) {
   paq_plan p;
   int rc = plan_prefill(d, cum_q_host, past_lens_host, &p);
   if (rc) return rc;
+  if (k_per_use && (p.path == PAQ_PATH_F32_PREFILL || d->kv_format == PAQ_KV_INT4 ||
+                    d->head_size != 128))
+    return fail(PAQ_ERR_UNSUPPORTED,
+                "the per-use K conversion variant covers 16-bit queries over 1-byte codes at "
+                "head size 128");
   if (p.path == PAQ_PATH_NONE) return PAQ_OK;
   if (padded_mql > 0 && padded_mql < p.max_query_len)
     return fail(PAQ_ERR_INVALID_ARG,
@@ -658,6 +663,7 @@ int run_prefill(const paq_desc* d, const void* query, void* out, const void* key
   if (rc) return rc;
   paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
                               block_table, cum_q, past_lens, softmax_scale, p);
+  a.pf_k_per_use = k_per_use ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   if (p.path == PAQ_PATH_PREFILL) {
     const int group = d->num_heads / d->kv_num_heads;
@@ -702,6 +708,17 @@ int32_t paged_attn_prefill_padded(const paq_desc* d, const void* query, void* ou
   if (max_query_len < 1) return fail(PAQ_ERR_INVALID_ARG, "max_query_len %d < 1", max_query_len);
   return run_prefill(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
                      past_lens, cum_q_host, past_lens_host, softmax_scale, max_query_len, stream);
+}
+
+int32_t paged_attn_prefill_k_per_use(const paq_desc* d, const void* query, void* out,
+                                     const void* key_cache, const void* value_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* cum_q,
+                                     const int32_t* past_lens, const int32_t* cum_q_host,
+                                     const int32_t* past_lens_host, float softmax_scale,
+                                     void* stream) {
+  return run_prefill(d, query, out, key_cache, value_cache, k_scale, v_scale, block_table, cum_q,
+                     past_lens, cum_q_host, past_lens_host, softmax_scale, 0, stream, true);
 }
 
 // ---- block-sparse prefill ----

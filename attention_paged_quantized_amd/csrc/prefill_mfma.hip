@@ -230,12 +230,21 @@ __device__ __attribute__((noinline)) long long prefill_find_item(const int32_t* 
   return -1;
 }
 
-template <int D, int KVF, int SM, typename TQ, typename TK, int NW>
+template <int D, int KVF, int SM, typename TQ, typename TK, int NW, bool KPU>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
   constexpr int kPfThreads = NW * 64;
   constexpr int kPfWaves = NW;
   using Geo = PfGeo<KVF, D, NW * 64>;
+  // KPU (the comparison variant of "INT8-KV Tensor-Core DynamicSparseAttention",
+  // section 1): K tiles are kept in LDS as raw 1-byte codes and every wave
+  // converts the operands it reads, instead of converting each tile once
+  // ("FlashInfer FP8 KV-cache prefill", repack section).  V is staged the
+  // same way in both (its operand takes 8 keys of one channel per lane, which
+  // the transposing 16-bit LDS read provides only from converted rows).
+  static_assert(!KPU || KVF != KV_INT4, "per-use K conversion: 1-byte formats only");
+  constexpr int KROW = KPU ? D + 16 : Geo::KROW;   // bytes of a K row in LDS
+  constexpr int KB = KPU ? 1 : 2;                  // bytes per K channel in LDS
   using MK = mfma32<TK>;
   typedef typename MK::vec kvec;
   constexpr int C = Geo::C;
@@ -364,14 +373,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   typedef uint32_t KWords[Geo::CPU / 2];
   auto stage_write = [&](int buf, int vpart, int i, const KWords& w) {   // unit i of this lane
     if (!k_active) return;
-    const int rowb = vpart ? Geo::VROW : Geo::KROW;
+    const int rowb = vpart ? Geo::VROW : KROW;
     const int c = vpart ? vc : kc;
-    uint8_t* rl = lds[buf] + (vpart ? kBN * Geo::KROW : 0) + (16 * wave + i * KPL + kx) * rowb;
+    uint8_t* rl = lds[buf] + (vpart ? kBN * KROW : 0) + (16 * wave + i * KPL + kx) * rowb;
     // channels [CPU*c, CPU*c + CPU) = 16-byte chunks CPU*c/8 ...
 #pragma unroll
     for (int j = 0; j < Geo::CPU / 8; ++j)
       *reinterpret_cast<u32x4*>(rl + 2 * Geo::CPU * c + 16 * j) =
           (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  };
+  auto stage_raw_k = [&](int buf, int i, const u32x4& w) {   // KPU: unit i as raw codes
+    if (!k_active) return;
+    *reinterpret_cast<u32x4*>(lds[buf] + (16 * wave + i * KPL + kx) * KROW + 16 * kc) = w;
   };
   // V codes of unit i of tile t as the PV operand
   auto v_decode = [&](const RawK& r, int t, int i, KWords& w) { decode_unit_v<KVF>(r.k[i], w); };
@@ -393,9 +406,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
   auto store_k = [&](const RawK& r, int buf) {
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
-      KWords w;
-      decode_unit<KVF, TK>(r.k[i], w);
-      stage_write(buf, 0, i, w);
+      if constexpr (KPU) {
+        stage_raw_k(buf, i, r.k[i]);
+      } else {
+        KWords w;
+        decode_unit<KVF, TK>(r.k[i], w);
+        stage_write(buf, 0, i, w);
+      }
     }
   };
   auto store_v = [&](const RawK& r, int t, int buf) {
@@ -457,19 +474,32 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
 
+  // K operand of one QK product: 8 channels of one key row, read from LDS
+  // as 16-bit values, or (KPU) as 8 raw codes converted here
+  using KOp = std::conditional_t<KPU, u32x2, kvec>;
+  auto kread = [&](const uint8_t* p) -> KOp { return *reinterpret_cast<const KOp*>(p); };
+  auto kop = [&](const KOp& x) -> kvec {
+    if constexpr (KPU) {
+      uint32_t w[8];
+      decode_unit<KVF, TK>((u32x4){x[0], x[1], 0u, 0u}, w);
+      return __builtin_bit_cast(kvec, (u32x4){w[0], w[1], w[2], w[3]});
+    } else {
+      return x;
+    }
+  };
   // (sched_group_barrier masks: 0x002 VALU, 0x008 MFMA, 0x100 LDS read,
   // 0x200 LDS write, 0x400 transcendental)
   // S^T = K Q'^T of tile t (keys 0-31 in s[0], 32-63 in s[1]), from LDS
   // buffer t & 1; the two accumulations alternate.
   auto qk = [&](int t, f32x16 (&s)[2]) {
-    const uint8_t* k0p = lds[t & 1] + n * Geo::KROW + 16 * eta;
-    const uint8_t* k1p = k0p + 32 * Geo::KROW;
+    const uint8_t* k0p = lds[t & 1] + n * KROW + 8 * KB * eta;
+    const uint8_t* k1p = k0p + 32 * KROW;
     s[0] = (f32x16){};
     s[1] = (f32x16){};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const kvec a0 = *reinterpret_cast<const kvec*>(k0p + 32 * kk);
-      const kvec a1 = *reinterpret_cast<const kvec*>(k1p + 32 * kk);
+      const kvec a0 = kop(kread(k0p + 16 * KB * kk));
+      const kvec a1 = kop(kread(k1p + 16 * KB * kk));
       s[0] = MK::run(a0, qop[kk], s[0]);
       s[1] = MK::run(a1, qop[kk], s[1]);
     }
@@ -540,9 +570,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     constexpr int NM = 2 * NKK;                     // products (16 for D = 128)
     const float bias = kPfPScaleLog2 - m_log;
     const f16x2 ones = (f16x2){(f16)1.0f, (f16)1.0f};
-    const uint8_t* k0p = lds[(t + 1) & 1] + n * Geo::KROW + 16 * eta;
-    auto kaddr = [&](int i) { return k0p + (i & 1) * 32 * Geo::KROW + 32 * (i >> 1); };
-    kvec ka[4];
+    const uint8_t* k0p = lds[(t + 1) & 1] + n * KROW + 8 * KB * eta;
+    auto kaddr = [&](int i) { return k0p + (i & 1) * 32 * KROW + 16 * KB * (i >> 1); };
+    KOp ka[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lp[i] = 0.f;
     __builtin_amdgcn_sched_barrier(0);
@@ -550,7 +580,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       s_next[0] = (f32x16){};
       s_next[1] = (f32x16){};
 #pragma unroll
-      for (int i = 0; i < 4 && i < NM; ++i) ka[i] = *reinterpret_cast<const kvec*>(kaddr(i));
+      for (int i = 0; i < 4 && i < NM; ++i) ka[i] = kread(kaddr(i));
     }
     // score pair j = scores 2j, 2j+1 of this lane (block j/8, registers
     // 2j%16, +1); bundle i forms the exponent of pair i+1, the powers of pair
@@ -570,8 +600,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (QK) {
         if (i < NM) {
-          s_next[i & 1] = MK::run(ka[i & 3], qop[i >> 1], s_next[i & 1]);
-          if (i + 4 < NM) ka[i & 3] = *reinterpret_cast<const kvec*>(kaddr(i + 4));
+          s_next[i & 1] = MK::run(kop(ka[i & 3]), qop[i >> 1], s_next[i & 1]);
+          if (i + 4 < NM) ka[i & 3] = kread(kaddr(i + 4));
         }
       }
       if (i > 0) finish(i - 1, y0, y1);
@@ -605,7 +635,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
     constexpr int NM = 4 * NDT;                     // products (16 for D = 128)
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const uint8_t* vb = lds[t & 1] + kBN * Geo::KROW + v_lane;
+    const uint8_t* vb = lds[t & 1] + kBN * KROW + v_lane;
     auto vread = [&](int i) -> f16x8 {
       const uint8_t* q = vb + 16 * (i & 3) * Geo::VROW + 64 * (i >> 2);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
@@ -626,8 +656,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(
       }
       // unit u: K decoded in bundle u and written in bundle u+1, V decoded in
       // bundle KL+1+u and written in bundle KL+2+u
-      if (i >= 1 && i <= KL) stage_write(t & 1, 0, i - 1, kw[(i - 1) & 1]);
-      if (i < KL) decode_unit<KVF, TK>(rk.k[i], kw[i & 1]);
+      if constexpr (KPU) {
+        if (i < KL) stage_raw_k(t & 1, i, rk.k[i]);
+      } else {
+        if (i >= 1 && i <= KL) stage_write(t & 1, 0, i - 1, kw[(i - 1) & 1]);
+        if (i < KL) decode_unit<KVF, TK>(rk.k[i], kw[i & 1]);
+      }
       if (i >= KL + 2 && i <= 2 * KL + 1) stage_write((t + 1) & 1, 1, i - KL - 2, vw[(i - KL - 2) & 1]);
       if (i >= KL + 1 && i <= 2 * KL) v_decode(rv, t + 1, i - KL - 1, vw[(i - KL - 1) & 1]);
       if (i == 15) {
@@ -710,8 +744,17 @@ static int launch_pf(const AttnArgs& a, hipStream_t st) {
   constexpr int NW = kPfWavesPerGroup;
   static_assert(NW == kPrefillWaves, "prefill geometry");
   dim3 grid(a.grid_x, 1, 1);                  // from the host plan (exact tile counts)
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW>), grid, dim3(NW * 64), 0, st,
-                     a, a.block_table);
+  if (a.pf_k_per_use) {
+    // the per-use conversion variant: 1-byte formats at head size 128
+    if constexpr (KVF != KV_INT4 && D == 128) {
+      hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW, true>), grid,
+                         dim3(NW * 64), 0, st, a, a.block_table);
+      return 0;
+    }
+    return -1;
+  }
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, KVF, SM, TQ, TK, NW, false>), grid, dim3(NW * 64),
+                     0, st, a, a.block_table);
   return 0;
 }
 

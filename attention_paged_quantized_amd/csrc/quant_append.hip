@@ -29,12 +29,14 @@ __global__ __launch_bounds__(kAppendThreads) void quant_append_kernel(
     const int32_t* __restrict__ cum_q, const int32_t* __restrict__ past_lens, int hkv,
     int head_size, int block_size, int max_blocks, int tokens_per_wg) {
   const int b = blockIdx.y;
+  // the lengths in one round trip (past is read before the exit test, so the
+  // row loads below wait for one memory latency, not two)
   const int q0 = cum_q[b];
   const int qlen = cum_q[b + 1] - q0;
+  const int past = past_lens[b];
   const int i_begin = blockIdx.x * tokens_per_wg;
   if (i_begin >= qlen) return;
   const int i_end = min(qlen, i_begin + tokens_per_wg);
-  const int past = past_lens[b];
   const int chunks_per_row = hkv * head_size / 8;           // per tensor
   const int chunk_per_tok = 2 * chunks_per_row;              // K and V
   const int C = (KVF == KV_INT4) ? head_size / 2 : head_size;

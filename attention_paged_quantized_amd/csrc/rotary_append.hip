@@ -99,10 +99,10 @@ __global__ __launch_bounds__(kRotThreads) void rotary_append_kernel(AppendArgs a
   const int b = blockIdx.y;
   const int q0 = a.cum_q[b];
   const int qlen = a.cum_q[b + 1] - q0;
+  const int past = a.past_lens[b];              // read beside the lengths
   const int i_begin = blockIdx.x * a.tokens_per_wg;
   if (i_begin >= qlen) return;
   const int i_end = min(qlen, i_begin + a.tokens_per_wg);
-  const int past = a.past_lens[b];
   const int D = a.head_size, rd = a.rotary_dim, hkv = a.hkv, half = rd / 2;
   const bool il = a.interleaved != 0;
   const int ur = il ? rd / 8 : rd / 16;                 // rotation units per head

@@ -15,9 +15,10 @@ time, GB/s), or the algorithmic MFMA rate (TFLOP/s, unmasked causal pairs
 only) for prefill.  `roofline` is measured for the attention call with HIP
 events on its stream.  Unless --only is given, `configs` holds the same
 measurement for the other four workloads (tiny_decode's latency in us
-included) and `ablations` the partition and grid comparisons: single pass
-against the automatic split on the two decode workloads, and the exact
-prefill grid against one sized from token_count - batch + 1.
+included) and `ablations` the comparisons: single pass against the automatic
+partition on the two decode workloads, the exact prefill grid against one
+sized from token_count - batch + 1, K codes converted once into LDS against
+converted by every wave at each use, and the block-sparse decode and prefill.
 """
 
 import argparse
@@ -68,15 +69,21 @@ def parse():
                          "WRITE_SIZE) into profiles/counters_<workload>.json and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--sparse", action="store_true",
-                    help="decode: block-sparse attention over a local window of 2 blocks plus "
-                         "every 3rd earlier block (paged_attn_decode_sparse); value counts the "
-                         "selected KV bytes")
+                    help="block-sparse attention: decode over a local window of 2 blocks plus "
+                         "every 3rd earlier block (paged_attn_decode_sparse); prefill over the "
+                         "blocks holding new tokens, the 2 before them and every 3rd earlier "
+                         "block (paged_attn_prefill_sparse); value counts the "
+                         "selected KV bytes (decode) or the visible pairs' flops (prefill)")
     ap.add_argument("--rotary", action="store_true",
                     help="the step's append is kv_quant_append_rotary (rotary embedding of "
                          "the new query and key rows over all head_size channels)")
     ap.add_argument("--padded-grid", action="store_true",
                     help="prefill: size the grid from token_count - batch + 1 for every "
                          "(sequence, kv head) pair (paged_attn_prefill_padded)")
+    ap.add_argument("--k-per-use", action="store_true",
+                    help="prefill: K codes kept raw in LDS and converted by every wave at "
+                         "each use (paged_attn_prefill_k_per_use), the staging scheme the "
+                         "default is compared with")
     ap.add_argument("--only", action="store_true",
                     help="measure the --workload alone (no configs / ablations)")
     return ap.parse_args()
@@ -98,9 +105,14 @@ def append_bytes(w, T, rotary):
     return int(n)
 
 
-def prefill_flops(w):
+def prefill_flops(w, num_sel=None):
+    """4 * D * H per visible (query, key) pair; with num_sel (block-sparse
+    prefill) a row sees the selected earlier blocks and its local blocks up
+    to itself: num_sel * bs + past % bs + i + 1 keys."""
     n = w.q_lens.astype(np.int64)
     p = w.past_lens.astype(np.int64)
+    if num_sel is not None:
+        p = np.asarray(num_sel, np.int64) * w.block_size + p % w.block_size
     pairs = (n * p + n * (n + 1) // 2).sum()
     return int(4 * w.head_size * w.num_heads * pairs)
 
@@ -389,7 +401,7 @@ _WORKLOADS = {}          # workloads built so far (the ablations reuse them)
 
 
 def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, warm=True,
-            append_loop=True):
+            append_loop=True, k_per_use=False):
     """Time `steps` steps (append + attention) of workload `name` after
     `warmup` untimed ones; returns the measurement as a dict, plus the
     workload, one filled Device and the descriptor (for the CPU figures)."""
@@ -431,9 +443,19 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
             ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     heuristic_mql = T - w.batch + 1
-    if sparse:
-        if kind != "decode":
-            sys.exit("--sparse applies to decode workloads")
+    if sparse and kind == "prefill":
+        # the 2 earlier blocks before the local ones + every 3rd earlier block
+        nfb = w.past_lens // w.block_size
+        rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in nfb]
+        sel_np = np.zeros((w.batch, max(1, max(len(r) for r in rows))), np.int32)
+        num_np = np.array([len(r) for r in rows], np.int32)
+        for b, r in enumerate(rows):
+            sel_np[b, :len(r)] = r
+        sel_d, num_d = torch.from_numpy(sel_np).to(dev), torch.from_numpy(num_np).to(dev)
+        nbytes = paq.paged_attn_prefill_sparse_workspace_size(desc, w.cum_q, w.past_lens,
+                                                              num_np, sel_np.shape[1])
+        ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
+    elif sparse:
         nbk = -(-(w.past_lens + 1) // w.block_size)
         rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in nbk]
         sel_np = np.zeros((w.batch, max(len(r) for r in rows)), np.int32)
@@ -457,6 +479,14 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
             paq.paged_attn_decode(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                   g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens, 0.0, S,
                                   ws, stream)
+        elif sparse:
+            paq.paged_attn_prefill_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
+                                          g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
+                                          sel_d, num_d, num_np, 0.0, ws, stream)
+        elif k_per_use:
+            paq.paged_attn_prefill_k_per_use(desc, g.query, out, g.kc, g.vc, g.k_scale,
+                                             g.v_scale, g.block_table, g.cum_q, g.past, w.cum_q,
+                                             w.past_lens, 0.0, stream)
         elif padded:
             paq.paged_attn_prefill_padded(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                           g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
@@ -585,16 +615,19 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                          "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
                          "algorithmic_bytes_per_launch": kvb}
     else:
-        fl = prefill_flops(w)
+        fl = prefill_flops(w, num_np if sparse else None)
         peak = MFMA_PEAK_TFLOPS[w.q_dtype]
         r.update({"value": round(fl / (ms_step / 1e3) / 1e12, 3), "unit": "TFLOP/s",
                   "tokens_per_s": round(T / (ms_step / 1e3), 1)})
         achieved = fl / (kern_avg / 1e3) / 1e12
         r["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                         "traffic": None if padded else counters(w.name, "prefill"),
-                         "kernel": "paged_attn_prefill%s call (prefill_mfma_kernel)" %
-                                   ("_padded" if padded else ""),
+                         "traffic": None if padded or sparse or k_per_use
+                         else counters(w.name, "prefill"),
+                         "kernel": "paged_attn_prefill%s call (%sprefill_mfma_kernel)" %
+                                   ("_padded" if padded else "_sparse" if sparse else
+                                    "_k_per_use" if k_per_use else "",
+                                    "sparse_prefill_compact_kernel + " if sparse else ""),
                          "kernel_us_avg": round(kern_avg * 1e3, 3),
                          "kernel_us_p10_p90": p10p90,
                          "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
@@ -612,9 +645,14 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                        "frac": round(ab / (app_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                        "traffic": counters(w.name, "rotary_append_kernel" if rotary
                                            else "quant_append_kernel")}
-    if sparse:
+    if sparse and kind == "decode":
         cfg["sparse"] = "2-block local window + every 3rd earlier block; %d of %d KV bytes" % (
             kvb, kv_bytes(w))
+    elif sparse:
+        cfg["sparse"] = ("the blocks holding new tokens + the 2 blocks before them + every 3rd "
+                         "earlier block; %d of %d causal (query, key) pairs" %
+                         (fl // (4 * w.head_size * w.num_heads),
+                          prefill_flops(w) // (4 * w.head_size * w.num_heads)))
     keep = devs[0]
     del devs, outs, ws
     torch.cuda.empty_cache()
@@ -656,7 +694,7 @@ def main():
     torch.cuda.set_device(0)
     paq.lib()
     r, w, g0, desc = measure(args, args.workload, splits=args.splits, padded=args.padded_grid,
-                             rotary=args.rotary, sparse=args.sparse)
+                             rotary=args.rotary, sparse=args.sparse, k_per_use=args.k_per_use)
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16"}.get(w.q_dtype, "f16"),
@@ -685,7 +723,7 @@ def main():
         torch.cuda.synchronize()
     del src, dst
 
-    if not args.only and not args.sparse and not args.rotary:
+    if not args.only and not args.sparse and not args.rotary and not args.k_per_use:
         # every configuration, then the ablations (short timings each)
         configs = {}
         for name in ("tiny_decode", "int8_decode", "int4_long", "int8_prefill", "fp8_prefill"):
@@ -702,7 +740,13 @@ def main():
                 ("int8_prefill grid from token_count - batch + 1", "int8_prefill",
                  {"padded": True}),
                 ("fp8_prefill grid from token_count - batch + 1", "fp8_prefill",
-                 {"padded": True})):
+                 {"padded": True}),
+                ("int8_prefill K codes converted per use", "int8_prefill", {"k_per_use": True}),
+                ("fp8_prefill K codes converted per use", "fp8_prefill", {"k_per_use": True}),
+                ("int8_decode block-sparse (2-block window + every 3rd block)", "int8_decode",
+                 {"sparse": True}),
+                ("int8_prefill block-sparse (local blocks + 2 before + every 3rd)",
+                 "int8_prefill", {"sparse": True})):
             ar = measure(args, name, warm=False, append_loop=False, **kw)[0]
             s = summary(ar)
             ref = configs[name]

@@ -7,7 +7,9 @@
  *                       (kv_quant_append_rotary: rotary embedding first);
  *   paged_attn_decode   GQA decode (one new token per sequence), single pass or
  *                       split-KV ("flash decoding") with a log-sum-exp merge;
- *   paged_attn_prefill  ragged, causal, chunked prefill;
+ *   paged_attn_prefill  ragged, causal, chunked prefill
+ *                       (paged_attn_prefill_padded, paged_attn_prefill_k_per_use:
+ *                       the grid and staging schemes it is compared with);
  *   paged_attn_decode_sparse  decode over caller-selected KV blocks;
  *   paged_attn_prefill_sparse prefill over caller-selected earlier blocks
  *                             plus the blocks holding the new tokens;
@@ -305,6 +307,25 @@ size_t paged_attn_decode_sparse_workspace_size(const paq_desc* d, const int32_t*
                                                const int32_t* past_lens_host,
                                                const int32_t* num_sel_host, int32_t max_sel,
                                                int32_t num_splits);
+
+/* paged_attn_prefill with the other staging scheme, for comparison: the pages
+ * disagree on where the 1-byte codes become 16-bit operands.  The default
+ * prefill converts every K and V tile once into LDS ("FlashInfer FP8 KV-cache
+ * prefill", repack section); this variant keeps the K tile in LDS as raw
+ * codes and lets every wave convert the operands it reads, after the LDS
+ * read ("INT8-KV Tensor-Core DynamicSparseAttention", section 1).  V is
+ * staged as in the default (its operand needs 8 keys of one channel per
+ * lane, which the transposing LDS read gives only from 16-bit rows).  Same
+ * arguments, results within the same tolerance of the exact attention.
+ * Returns PAQ_ERR_UNSUPPORTED (nothing launched) unless the query is 16-bit,
+ * the format INT8 or FP8 E4M3 and head_size 128. */
+int32_t paged_attn_prefill_k_per_use(const paq_desc* d, const void* query, void* out,
+                                     const void* key_cache, const void* value_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* cum_q,
+                                     const int32_t* past_lens, const int32_t* cum_q_host,
+                                     const int32_t* past_lens_host, float softmax_scale,
+                                     void* stream);
 
 /* Block-sparse prefill ("INT8-KV Tensor-Core DynamicSparseAttention",
  * section 1, which names prefill beside decode; the page gives no selection

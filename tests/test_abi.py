@@ -350,6 +350,21 @@ def test_sparse_prefill_checks():
     assert rc == paq.PAQ_ERR_INVALID_ARG and "sel_blocks" in paq.paq_last_error()
 
 
+def test_prefill_k_per_use_refusals():
+    """The per-use K conversion variant exists for 16-bit queries over 1-byte
+    codes at head size 128; anything else is refused before launch."""
+    L = paq.lib()
+    cum, past = [0, 5], [10]
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    for kw in ({"fmt": "int4"}, {"D": 64}, {"q": "f32"}):
+        d = _desc(1, 5, **kw)
+        rc = L.paged_attn_prefill_k_per_use(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, pa, pb, 0.0, None)
+        assert rc == paq.PAQ_ERR_UNSUPPORTED, kw
+        assert "per-use" in paq.paq_last_error()
+
+
 def test_noalloc_decode_refuses_plans_beyond_its_scratch():
     """The allocation-free decode holds 16 MiB of scratch per GPU: a plan that
     needs more is refused before anything is launched (no GPU involved)."""

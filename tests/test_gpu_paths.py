@@ -225,3 +225,40 @@ def test_prefill_padded_grid_matches_exact(name):
     with pytest.raises(paq.PaqError) as e:
         paq.paged_attn_prefill_padded(*args, int(w.q_lens.max()) - 1)
     assert e.value.status == paq.PAQ_ERR_INVALID_ARG
+
+
+def _k_per_use_case(w):
+    import torch
+    from tests.gpu_cases import desc_for
+    g = Device(w).fill()
+    exact = g.attend()
+    out = torch.full_like(exact, float("nan"))
+    paq.paged_attn_prefill_k_per_use(desc_for(w, w.token_count), g.query, out, g.kc, g.vc,
+                                     g.k_scale, g.v_scale, g.block_table, g.cum_q, g.past,
+                                     w.cum_q, w.past_lens)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(w)
+    compare.check(out.float().cpu().numpy(), oracle_attention(w, kc, vc), w.q_dtype, w.name)
+    # the same exact 16-bit operands in the same products: identical output
+    assert torch.equal(out, exact)
+
+
+@pytest.mark.parametrize("name", ["int8_prefill_small", "fp8_prefill_small"])
+def test_prefill_k_per_use_matches(name):
+    """The comparison staging scheme (K codes raw in LDS, converted by every
+    wave at each use) against the oracle, and bit-identical to the default
+    (convert once) path."""
+    print("case k per use", name, flush=True)
+    _k_per_use_case(workloads.make(name))
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("qdt", ["f16", "bf16"])
+@pytest.mark.parametrize("mode", ["channel", "head"])
+def test_prefill_k_per_use_formats(fmt, qdt, mode):
+    print("case k per use", fmt, qdt, mode, flush=True)
+    w = workloads.custom("kpu", 41, batch=4, num_heads=16, kv_num_heads=4, head_size=128,
+                         block_size=32, past=np.array([0, 77, 150, 5]),
+                         q_lens=np.array([70, 0, 101, 33]), q_dtype=qdt, kv_format=fmt,
+                         scale_mode=mode, kind="prefill")
+    _k_per_use_case(w)
