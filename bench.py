@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then "
                          "WRITE_SIZE) into profiles/counters_<workload>.json and exit")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="no GPU: turn a rocprofv3 --pmc run of the MFMA counters (" +
+                         " ".join(MFMA_COUNTERS) + ") over a prefill workload into "
+                         "profiles/prefill_mfma_kernel_<workload>_mfma.json and exit")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--sparse", action="store_true",
                     help="block-sparse attention: decode over a local window of 2 blocks plus "
@@ -238,15 +242,17 @@ def cpu_baseline(w, seconds):
 
 
 # Kernels of one attention call, by workload kind (substrings of the symbol).
-CALL_KERNELS = {"decode": ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel"),
-                "prefill": ("prefill_mfma_kernel", "attn_f32_kernel")}
+CALL_KERNELS = {"decode": ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel",
+                           "sparse_compact_kernel"),
+                "prefill": ("prefill_mfma_kernel", "attn_f32_kernel",
+                            "sparse_prefill_compact_kernel")}
 CALIB_KERNEL = "neg_kernel"
 
 
 def _short(name):
     for k in ("decode_stream_kernel", "combine_kernel", "attn_f32_kernel",
               "prefill_mfma_kernel", "quant_append_kernel", "rotary_append_kernel",
-              CALIB_KERNEL):
+              "sparse_prefill_compact_kernel", "sparse_compact_kernel", CALIB_KERNEL):
         if k in name:
             return k
     return name[:48]
@@ -262,8 +268,10 @@ def summarize_stats(args):
     if args.rotary:
         return summarize_append_stats(args, w, rows, "rotary_append_kernel")
     call = [r for r in rows if any(k in r["Name"] for k in CALL_KERNELS[w.kind])]
-    main_k = _short(call[0]["Name"]) if call else "none"
-    lines = ["rocprofv3 kernel statistics, workload %s (%s)" % (w.name, w.kind),
+    main = [r for r in call if "compact" not in r["Name"]]
+    main_k = _short(main[0]["Name"]) if main else "none"
+    lines = ["rocprofv3 kernel statistics, workload %s (%s)%s" %
+             (w.name, w.kind, (", variant " + variant(args)[1:]) if variant(args) else ""),
              "command: %s" % (args.command or "(not recorded)"),
              "kernel sources sha256[:16]: %s" % source_sha(w.kind), "",
              "%-22s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us",
@@ -275,16 +283,18 @@ def summarize_stats(args):
     tot = sum(float(r["AverageNs"]) for r in call) / 1e3
     lines += ["", "attention call (%s): %.3f us average per call" %
               (" + ".join(_short(r["Name"]) for r in call), tot)]
+    if args.sparse:
+        sel, num = sparse_selection(w)
     if w.kind == "decode":
-        kvb = kv_bytes(w)
+        kvb = sparse_kv_bytes(w, sel, num) if args.sparse else kv_bytes(w)
         lines.append("algorithmic KV bytes per call %d -> %.1f GB/s, %.4f of 8000 GB/s" %
                      (kvb, kvb / (tot * 1e3), kvb / (tot * 1e3) / HBM_PEAK_GBS))
     else:
-        fl = prefill_flops(w)
+        fl = prefill_flops(w, num if args.sparse else None)
         lines.append("algorithmic flops per call %d -> %.1f TFLOP/s, %.4f of %.1f" %
                      (fl, fl / (tot * 1e-6) / 1e12, fl / (tot * 1e-6) / 1e12 /
                       MFMA_PEAK_TFLOPS[w.q_dtype], MFMA_PEAK_TFLOPS[w.q_dtype]))
-    out = os.path.join(ROOT, "profiles", "%s_%s.txt" % (main_k, w.name))
+    out = os.path.join(ROOT, "profiles", "%s_%s%s.txt" % (main_k, w.name, variant(args)))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote", out)
@@ -314,6 +324,54 @@ def summarize_append_stats(args, w, rows, kernel):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote", out)
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+                 "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(args):
+    """One rocprofv3 --pmc run of MFMA_COUNTERS over a prefill workload ->
+    profiles/prefill_mfma_kernel_<workload>[variant]_mfma.json: matrix-core
+    busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs x the
+    per-XCD active cycles), the MFMA flops issued (MOPS x 512) against the
+    algorithmic flops, and the VALU-active fraction, medians over dispatches."""
+    import csv
+    import glob
+    import workloads
+    w = workloads.make(args.workload)
+    vals = {}
+    for f in glob.glob(os.path.join(args.summarize_mfma, "**", "*counter_collection.csv"),
+                       recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "prefill_mfma_kernel" in r["Kernel_Name"] and r["Counter_Name"] in MFMA_COUNTERS:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+    n_xcd, cus = 8, 256
+    active = med["GRBM_GUI_ACTIVE"] / n_xcd             # cycles the kernel kept the GPU busy
+    mops = med.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    fl = prefill_flops(w, sparse_selection(w)[1] if args.sparse else None)
+    res = {"workload": w.name, "variant": variant(args)[1:] or "default",
+           "source_sha": source_sha("prefill"), "command": args.command,
+           "dispatches": len(vals.get("GRBM_GUI_ACTIVE", [])),
+           "counters_median": med,
+           "mfma_busy_frac": round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * cus * 4), 4),
+           "valu_active_frac": round(med["SQ_ACTIVE_INST_VALU"] / (active * cus), 4)
+           if "SQ_ACTIVE_INST_VALU" in med else None,
+           "mfma_flops_issued": mops * 512,
+           "algorithmic_flops": fl,
+           "issued_over_algorithmic": round(mops * 512 / fl, 4),
+           "active_cycles_per_xcd": active,
+           "definitions": "mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x "
+                          "256 CU x 4 SIMD); valu_active_frac = SQ_ACTIVE_INST_VALU / "
+                          "(GRBM_GUI_ACTIVE / 8 x 256); flops issued = MOPS x 512 (the "
+                          "profiler's MFMA FLOPs unit)"}
+    out = os.path.join(ROOT, "profiles", "prefill_mfma_kernel_%s%s_mfma.json" %
+                       (w.name, variant(args)))
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print("wrote", out, json.dumps(res))
 
 
 def summarize_pmc(args):
@@ -352,10 +410,12 @@ def summarize_pmc(args):
     hbm = (res["fetch_kib"] * ff + res["write_kib"] * wf) * 1024
     res["hbm_bytes_per_call"] = int(hbm)
     if w.kind == "decode":
-        res["algorithmic_kv_bytes_per_call"] = kv_bytes(w)
-        res["traffic_over_algorithmic"] = round(hbm / kv_bytes(w), 4)
+        kvb = sparse_kv_bytes(w, *sparse_selection(w)) if args.sparse else kv_bytes(w)
+        res["algorithmic_kv_bytes_per_call"] = kvb
+        res["traffic_over_algorithmic"] = round(hbm / kvb, 4)
     if ks:
-        out = os.path.join(ROOT, "profiles", "%s_%s_counters.json" % (ks[0], w.name))
+        out = os.path.join(ROOT, "profiles", "%s_%s%s_counters.json" % (ks[0], w.name,
+                                                                          variant(args)))
         with open(out, "w") as f:
             json.dump(res, f, indent=1)
         print("wrote", out, json.dumps(res))
@@ -378,6 +438,48 @@ def summarize_pmc(args):
 
 
 CALIB_ELEMS = 2 ** 26          # fp32 elements of the counter-calibration copy (256 MiB)
+
+
+def sparse_selection(w):
+    """The benched block-sparse selections, (sel (batch, max_sel), num (batch)):
+    decode, a 2-block local window plus every 3rd earlier block of each
+    sequence; prefill, the 2 blocks before the ones holding new tokens plus
+    every 3rd earlier block (the local blocks are always attended)."""
+    if w.kind == "decode":
+        n_all = -(-(w.past_lens + 1) // w.block_size)
+    else:
+        n_all = w.past_lens // w.block_size
+    rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in n_all]
+    sel = np.zeros((w.batch, max(1, max(len(r) for r in rows))), np.int32)
+    num = np.array([len(r) for r in rows], np.int32)
+    for b, r in enumerate(rows):
+        sel[b, :len(r)] = r
+    return sel, num
+
+
+def sparse_kv_bytes(w, sel, num):
+    """Selected KV bytes of a block-sparse decode (whole blocks, the last one up
+    to kv_len), over the sequences with a new row."""
+    keys = 0
+    for b in range(w.batch):
+        if w.q_lens[b] > 0:
+            keys += sum(min(w.block_size, int(w.past_lens[b]) + 1 - w.block_size * int(x))
+                        for x in sel[b, :num[b]])
+    return keys * w.kv_num_heads * 2 * w.cache_head_size
+
+
+def variant(args):
+    """File-name suffix of a profiled variant ("" for the default call)."""
+    v = ""
+    if args.splits is not None:
+        v += "_splits%d" % args.splits
+    if args.padded_grid:
+        v += "_padded"
+    if args.k_per_use:
+        v += "_k_per_use"
+    if args.sparse:
+        v += "_sparse"
+    return v
 
 
 def sleep_rate(stream):
@@ -444,31 +546,17 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
     stream = torch.cuda.current_stream()
     heuristic_mql = T - w.batch + 1
     if sparse and kind == "prefill":
-        # the 2 earlier blocks before the local ones + every 3rd earlier block
-        nfb = w.past_lens // w.block_size
-        rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in nfb]
-        sel_np = np.zeros((w.batch, max(1, max(len(r) for r in rows))), np.int32)
-        num_np = np.array([len(r) for r in rows], np.int32)
-        for b, r in enumerate(rows):
-            sel_np[b, :len(r)] = r
+        sel_np, num_np = sparse_selection(w)
         sel_d, num_d = torch.from_numpy(sel_np).to(dev), torch.from_numpy(num_np).to(dev)
         nbytes = paq.paged_attn_prefill_sparse_workspace_size(desc, w.cum_q, w.past_lens,
                                                               num_np, sel_np.shape[1])
         ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
     elif sparse:
-        nbk = -(-(w.past_lens + 1) // w.block_size)
-        rows = [sorted(set(list(range(max(0, n - 2), n)) + list(range(0, n, 3)))) for n in nbk]
-        sel_np = np.zeros((w.batch, max(len(r) for r in rows)), np.int32)
-        num_np = np.array([len(r) for r in rows], np.int32)
-        for b, r in enumerate(rows):
-            sel_np[b, :len(r)] = r
+        sel_np, num_np = sparse_selection(w)
         sel_d, num_d = torch.from_numpy(sel_np).to(dev), torch.from_numpy(num_np).to(dev)
         nbytes = paq.paged_attn_decode_sparse_workspace_size(desc, w.cum_q, w.past_lens, num_np,
                                                              sel_np.shape[1], S)
         ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
-        # selected keys: whole blocks, the last one up to kv_len
-        sel_keys = [sum(min(w.block_size, int(w.past_lens[b]) + 1 - w.block_size * x) for x in r)
-                    for b, r in enumerate(rows)]
 
     def attention(g, out):
         if kind == "decode" and sparse:
@@ -591,9 +679,7 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
     if kind == "decode":
         kvb = kv_bytes(w)
         if sparse:
-            act = w.q_lens > 0
-            kvb = int(sum(k for k, a in zip(sel_keys, act) if a)) * w.kv_num_heads * 2 * \
-                w.cache_head_size
+            kvb = sparse_kv_bytes(w, sel_np, num_np)
         act = int((w.q_lens > 0).sum())
         r.update({"value": round(kvb / (ms_step / 1e3) / 1e9, 2), "unit": "GB/s",
                   "tokens_per_s": round(act / (ms_step / 1e3), 1),
@@ -681,6 +767,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
