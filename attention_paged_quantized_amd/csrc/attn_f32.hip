@@ -67,7 +67,9 @@ __device__ __forceinline__ float code_at(const uint8_t* row, int d) {
   }
 }
 
-template <int KVF, int SM, typename TQ>
+// MG: the largest GQA group the instance serves (4 or 16): loops over the
+// group and the LDS arrays are sized by it, so small groups run short code.
+template <int KVF, int SM, typename TQ, int MG>
 __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int r = blockIdx.x;
   const int g = blockIdx.y;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   // scale (for the normaliser) and its query elements with their scales.
   const float ks_mine = (SM == SCALE_CHANNEL) ? (tid < D ? fabsf(a.k_scale[g * D + tid]) : 0.f)
                                               : fabsf(a.k_scale[g]);
-  constexpr int kQPer = kF32MaxGroup * kF32MaxD / kF32Threads;
+  constexpr int kQPer = MG * kF32MaxD / kF32Threads;
   const TQ* q = reinterpret_cast<const TQ*>(a.query);
   float qv[kQPer], sv[kQPer];
 #pragma unroll
@@ -119,9 +121,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int kend = min(visible, (int)(((long)(chunk + 1) * nb) / S) * bs);
   const int32_t* table = a.block_table + (size_t)b * a.max_blocks;
 
-  __shared__ float qs[kF32MaxGroup][kF32MaxD];
-  __shared__ float sc[kF32MaxGroup][kF32Threads];
-  __shared__ float m_sh[kF32MaxGroup], l_sh[kF32MaxGroup], alpha_sh[kF32MaxGroup];
+  __shared__ float qs[MG][kF32MaxD];
+  __shared__ float sc[MG][kF32Threads];
+  __shared__ float m_sh[MG], l_sh[MG], alpha_sh[MG];
   __shared__ int e_sh;
   __shared__ __attribute__((aligned(16))) uint8_t vrows[kF32Threads * (kF32MaxD + 16)];
 
@@ -140,9 +142,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int nslice = kF32Threads / D;
   const int my_d = tid % D;
   const int my_slice = tid / D;
-  float acc[kF32MaxGroup];
+  float acc[MG];
 #pragma unroll
-  for (int hh = 0; hh < kF32MaxGroup; ++hh) acc[hh] = 0.f;
+  for (int hh = 0; hh < MG; ++hh) acc[hh] = 0.f;
   __syncthreads();
 
   const int vst = C + 16;                 // LDS value row stride (16-byte aligned, padded)
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     // one key per thread: its key and value rows are loaded together (every
     // unit in flight at once), the value row goes to LDS for the weighted sum
     const int j = base + tid;
-    float dot[kF32MaxGroup];
+    float dot[MG];
 #pragma unroll
-    for (int hh = 0; hh < kF32MaxGroup; ++hh) dot[hh] = 0.f;
+    for (int hh = 0; hh < MG; ++hh) dot[hh] = 0.f;
     if (j < kend) {
       const int blk = table[j / bs];
       const size_t off = (((size_t)blk * bs + j % bs) * hkv + g) * C;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
         float k[16];
         codes16<KVF>(kw, 16 * u, k);
 #pragma unroll
-        for (int hh = 0; hh < kF32MaxGroup; ++hh) {
+        for (int hh = 0; hh < MG; ++hh) {
           if (hh < G) {
             float s = dot[hh];
 #pragma unroll
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < kF32MaxGroup; ++hh)
+    for (int hh = 0; hh < MG; ++hh)
       if (hh < G) sc[hh][tid] = (j < kend) ? dot[hh] : -INFINITY;   // raw scores
     __syncthreads();
     // per-head chunk maximum -> new running max and rescale factor
@@ -215,14 +217,14 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     // probability-weighted values: thread (slice, channel)
     if (my_slice < nslice) {
 #pragma unroll
-      for (int hh = 0; hh < kF32MaxGroup; ++hh)
+      for (int hh = 0; hh < MG; ++hh)
         if (hh < G) acc[hh] *= alpha_sh[hh];
       const int jn = min(kend - base, kF32Threads);
 #pragma unroll 4
       for (int t = my_slice; t < jn; t += nslice) {
         const float v = code_at<KVF>(vrows + t * vst, my_d);
 #pragma unroll
-        for (int hh = 0; hh < kF32MaxGroup; ++hh)
+        for (int hh = 0; hh < MG; ++hh)
           if (hh < G) acc[hh] = fmaf(sc[hh][t], v, acc[hh]);
       }
     }
@@ -234,13 +236,13 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   for (int s = 1; s < nslice; ++s) {
     if (my_slice == s) {
 #pragma unroll
-      for (int hh = 0; hh < kF32MaxGroup; ++hh)
+      for (int hh = 0; hh < MG; ++hh)
         if (hh < G) scratch[hh * D + my_d] = acc[hh];
     }
     __syncthreads();
     if (my_slice == 0) {
 #pragma unroll
-      for (int hh = 0; hh < kF32MaxGroup; ++hh)
+      for (int hh = 0; hh < MG; ++hh)
         if (hh < G) acc[hh] += scratch[hh * D + my_d];
     }
     __syncthreads();
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   if (my_slice != 0) return;
   const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[g * D + my_d] : a.v_scale[g];
 #pragma unroll
-  for (int hh = 0; hh < kF32MaxGroup; ++hh) {
+  for (int hh = 0; hh < MG; ++hh) {
     if (hh >= G) break;
     const int h = g * G + hh;
     const float l = l_sh[hh];
@@ -271,26 +273,32 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int KVF, int SM>
+template <int KVF, int SM, int MG>
 static int launch_q(const AttnArgs& a, dim3 grid, hipStream_t st) {
   switch (a.q_dtype) {
-    case DT_F32: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, float>), grid, dim3(kF32Threads), 0, st, a); return 0;
-    case DT_F16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, f16>), grid, dim3(kF32Threads), 0, st, a); return 0;
-    case DT_BF16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, bf16>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_F32: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, float, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_F16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, f16, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_BF16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, bf16, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
   }
   return -1;
+}
+
+template <int KVF, int SM>
+static int launch_g(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  return a.num_heads / a.hkv <= 4 ? launch_q<KVF, SM, 4>(a, grid, st)
+                                  : launch_q<KVF, SM, kF32MaxGroup>(a, grid, st);
 }
 
 int launch_decode_f32(const AttnArgs& a, hipStream_t st) {
   if (a.num_heads / a.hkv > kF32MaxGroup || a.head_size > kF32MaxD || a.token_count == 0) return -1;
   dim3 grid(a.token_count, a.hkv, a.num_splits);
   switch (a.kv_format * 2 + a.scale_mode) {
-    case KV_INT8 * 2 + SCALE_CHANNEL: return launch_q<KV_INT8, SCALE_CHANNEL>(a, grid, st);
-    case KV_INT8 * 2 + SCALE_HEAD: return launch_q<KV_INT8, SCALE_HEAD>(a, grid, st);
-    case KV_INT4 * 2 + SCALE_CHANNEL: return launch_q<KV_INT4, SCALE_CHANNEL>(a, grid, st);
-    case KV_INT4 * 2 + SCALE_HEAD: return launch_q<KV_INT4, SCALE_HEAD>(a, grid, st);
-    case KV_FP8 * 2 + SCALE_CHANNEL: return launch_q<KV_FP8, SCALE_CHANNEL>(a, grid, st);
-    case KV_FP8 * 2 + SCALE_HEAD: return launch_q<KV_FP8, SCALE_HEAD>(a, grid, st);
+    case KV_INT8 * 2 + SCALE_CHANNEL: return launch_g<KV_INT8, SCALE_CHANNEL>(a, grid, st);
+    case KV_INT8 * 2 + SCALE_HEAD: return launch_g<KV_INT8, SCALE_HEAD>(a, grid, st);
+    case KV_INT4 * 2 + SCALE_CHANNEL: return launch_g<KV_INT4, SCALE_CHANNEL>(a, grid, st);
+    case KV_INT4 * 2 + SCALE_HEAD: return launch_g<KV_INT4, SCALE_HEAD>(a, grid, st);
+    case KV_FP8 * 2 + SCALE_CHANNEL: return launch_g<KV_FP8, SCALE_CHANNEL>(a, grid, st);
+    case KV_FP8 * 2 + SCALE_HEAD: return launch_g<KV_FP8, SCALE_HEAD>(a, grid, st);
   }
   return -1;
 }
