@@ -2,9 +2,11 @@
 // gfx950 matrix cores (v_mfma_f32_16x16x32_f16), single pass or split-KV.
 //
 // Work unit: a wave streams 32-key tiles of a key range for HW adjacent kv
-// heads (HW = 128 / row bytes, so every copied row segment is a whole 128-byte
-// line) with its own online softmax; the 8 waves of a workgroup take the
-// tiles of a key range in turn and merge through LDS at its end.
+// heads (HW = min(2, 128 / row bytes): whole 128-byte lines per copied row
+// segment for 64-byte rows; the 32-byte rows of INT4 at head size 64 are
+// copied as 64-byte segments, since four heads per wave need more registers
+// than a wave has) with its own online softmax; the 8 waves of a workgroup
+// take the tiles of a key range in turn and merge through LDS at its end.
 // Decode is HBM-bound (every K/V byte is read once -- "GQA GEMV decode",
 // why-it-is-good item 1), so the design streams the raw codes HBM -> LDS with
 // whole-line non-temporal DMA copies, reads each lane's operand bytes from
