@@ -212,6 +212,10 @@ def paged_attn_decode_workspace_size(desc, cum_q_host, past_lens_host, num_split
 def paged_attn_decode(desc, query, out, key_cache, value_cache, k_scale, v_scale, block_table,
                       cum_q, past_lens, cum_q_host, past_lens_host, softmax_scale=0.0,
                       num_splits=0, workspace=None, stream=None):
+    """GQA decode through the C ABI.  `workspace` (device tensor of at least
+    paged_attn_decode_workspace_size() bytes, or None for a single pass) must
+    be zero-filled when allocated: its leading arrival counters have to be
+    zero when a split call starts, and every call leaves them zero."""
     a, pa = _host_i32(cum_q_host)
     b, pb = _host_i32(past_lens_host)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -170,10 +170,13 @@ const char* paq_last_error(void);
  *   -N length-balanced over N workgroups (N <= 256): the 32-key tiles of all
  *      (sequence, head group) pairs are dealt out in N equal contiguous runs,
  *      so every workgroup streams the same bytes whatever the lengths;
- *   0  automatic: length-balanced over about one workgroup per compute unit
- *      while the (sequence, head group) pairs alone would give fewer than four
- *      per compute unit (the flash-decoding rule of the same section, which
- *      splits when batch x heads under-fills the machine), else single pass.
+ *   0  automatic (the flash-decoding rule of the same section: split only
+ *      when batch x heads under-fills the machine): single pass while the
+ *      (sequence, head group) pairs fill the compute units or no sequence has
+ *      more than one block; otherwise, with skewed lengths (longest > 1.5 x
+ *      mean and >= 512 keys) length-balanced over about one workgroup per
+ *      compute unit, else S block-aligned chunks (about two workgroups per
+ *      compute unit, chunks of at least 256 keys).
  * Split and balanced calls merge partial results inside the same launch.
  * num_cus <= 0 plans for the current device (256 compute units when no device
  * is visible).  Returns a status; fills *plan on success. */
@@ -192,14 +195,20 @@ size_t paged_attn_decode_workspace_size(const paq_desc* d, const int32_t* cum_q_
                                         const int32_t* past_lens_host,
                                         int32_t num_splits);
 
-/* GQA paged decode: every q_len_b must be 0 or 1.  Split-KV (path SPLIT) needs
- * `workspace` (device, 16-byte aligned) of at least
- * paged_attn_decode_workspace_size() bytes; it holds fp32 partial outputs and
- * log-sum-exps (one per output row, head and slice of plan.grid_z: a
- * workgroup of the 16-bit kernel merges its chunks first) and is overwritten.  fp32 queries take the portable fp32
- * kernel; fp16/bf16 queries take the MFMA kernel, which folds the per-channel
- * k_scale into the query ("ONNX Runtime: INT4 Paged KV Cache", section 3).
- * Returns PAQ_ERR_WORKSPACE if the workspace is missing or too small. */
+/* GQA paged decode: every q_len_b must be 0 or 1.  fp32 queries take the
+ * portable fp32 kernel; fp16/bf16 queries take the MFMA kernel, which folds
+ * the per-channel k_scale into the query ("ONNX Runtime: INT4 Paged KV Cache",
+ * section 3).
+ * Workspace: split, length-balanced and fp32-split calls need `workspace`
+ * (device, 16-byte aligned) of at least paged_attn_decode_workspace_size()
+ * bytes (single-pass calls need none).  Its first 64 KiB are int32 arrival
+ * counters that MUST be zero when the call starts: zero the workspace once
+ * when it is allocated; every call leaves the counters zero again, so the
+ * same workspace serves any number of calls ordered on one stream (calls that
+ * overlap must use different workspaces).  The rest holds the partial results
+ * (per piece: a normalised fp32 output and its raw maximum and sum) and is
+ * overwritten.  Returns PAQ_ERR_WORKSPACE if the workspace is missing or too
+ * small. */
 int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
                           const void* key_cache, const void* value_cache,
                           const float* k_scale, const float* v_scale,
@@ -289,8 +298,11 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
  * and effective key counts, then the dense decode kernels over it (single
  * pass or split-KV with num_splits as for paged_attn_decode, planned on
  * num_sel_host * block_size keys).  `workspace` (device, 16-byte aligned)
- * must hold paged_attn_decode_sparse_workspace_size() bytes; it is
- * overwritten.  Otherwise as paged_attn_decode. */
+ * must hold paged_attn_decode_sparse_workspace_size() bytes: the compact
+ * table at its head is overwritten, and the rest is a paged_attn_decode
+ * workspace with the same rule (arrival counters zero when a split call
+ * starts, left zero: zero the whole workspace once when it is allocated).
+ * Otherwise as paged_attn_decode. */
 int32_t paged_attn_decode_sparse(const paq_desc* d, const void* query, void* out,
                                  const void* key_cache, const void* value_cache,
                                  const float* k_scale, const float* v_scale,
