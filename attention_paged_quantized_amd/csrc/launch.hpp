@@ -84,9 +84,10 @@ enum { DEC_SINGLE = 0, DEC_CHUNKS = 1, DEC_STREAM = 2 };
 // Arrival counters at the head of every decode workspace: one int32 per
 // (sequence, head group) of a split call, zero before a call and after it.
 constexpr int kDecCounters = 16384;
-// Pieces one segment may be cut into (the last one to arrive merges them all
-// at once: their weights must fit its LDS); the stream partition uses at most
-// this many workgroups.
+// Parts per sequence of the chunk partition, and workgroups of the balanced
+// (stream) partition: at most about one per compute unit is useful (more
+// workgroups per segment were measured slower), and the last piece to arrive
+// reads the others' partials in rounds of 16.
 constexpr int kDecMaxPartsPerSeq = 256;
 constexpr size_t kDecCounterBytes = (size_t)kDecCounters * 4;
 // Prefill (MFMA): workgroups of 4 waves x 32 / group tokens.  (Sequence, kv

@@ -122,10 +122,17 @@ def prefill_flops(w, num_sel=None):
 
 
 def source_sha(kind):
+    """Hash of the code of a kernel's sources, comments and whitespace left
+    out: a counter file stays valid across comment edits and goes stale when
+    the code changes."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "attention_paged_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "attention_paged_quantized_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)     # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
