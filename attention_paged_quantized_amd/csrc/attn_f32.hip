@@ -220,8 +220,28 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       for (int hh = 0; hh < MG; ++hh)
         if (hh < G) acc[hh] *= alpha_sh[hh];
       const int jn = min(kend - base, kF32Threads);
-#pragma unroll 4
-      for (int t = my_slice; t < jn; t += nslice) {
+      // four keys per step with all their LDS reads issued first (the stride
+      // is a run-time value, so the compiler does not unroll this itself),
+      // then the rest one at a time; the sums run in key order either way
+      int t = my_slice;
+      for (; t + 3 * nslice < jn; t += 4 * nslice) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = code_at<KVF>(vrows + (t + u * nslice) * vst, my_d);
+#pragma unroll
+        for (int hh = 0; hh < MG; ++hh) {
+          if (hh < G) {
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = sc[hh][t + u * nslice];
+            float s = acc[hh];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s = fmaf(w[u], v[u], s);
+            acc[hh] = s;
+          }
+        }
+      }
+      for (; t < jn; t += nslice) {
         const float v = code_at<KVF>(vrows + t * vst, my_d);
 #pragma unroll
         for (int hh = 0; hh < MG; ++hh)
@@ -231,23 +251,22 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // merge the key slices (reuse sc as [slice][G][D] scratch; G*D <= 16*128)
+  // merge the key slices in one exchange: slices 1.. write their sums to sc
+  // reused as [slice - 1][G][D] scratch ((nslice - 1) * G * D <= MG * 256
+  // floats, since nslice * D = 256), then slice 0 adds them in slice order
   float* scratch = &sc[0][0];
-  for (int s = 1; s < nslice; ++s) {
-    if (my_slice == s) {
+  if (my_slice > 0 && my_slice < nslice) {
 #pragma unroll
-      for (int hh = 0; hh < MG; ++hh)
-        if (hh < G) scratch[hh * D + my_d] = acc[hh];
-    }
-    __syncthreads();
-    if (my_slice == 0) {
-#pragma unroll
-      for (int hh = 0; hh < MG; ++hh)
-        if (hh < G) acc[hh] += scratch[hh * D + my_d];
-    }
-    __syncthreads();
+    for (int hh = 0; hh < MG; ++hh)
+      if (hh < G) scratch[((my_slice - 1) * G + hh) * D + my_d] = acc[hh];
   }
+  __syncthreads();
   if (my_slice != 0) return;
+  for (int sl = 1; sl < nslice; ++sl) {
+#pragma unroll
+    for (int hh = 0; hh < MG; ++hh)
+      if (hh < G) acc[hh] += scratch[((sl - 1) * G + hh) * D + my_d];
+  }
   const float vs = (SM == SCALE_CHANNEL) ? a.v_scale[g * D + my_d] : a.v_scale[g];
 #pragma unroll
   for (int hh = 0; hh < MG; ++hh) {
