@@ -597,9 +597,12 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
   __shared__ float sm_ml[NW][HW][2][kDecMaxGroup];        // running max, sum per wave
   __shared__ float sm_c2[HW];
   __shared__ int sm_last;
+  __shared__ int progress[NW];                            // tiles each wave has computed
   uint8_t* myring = ring[wave];
   WC cp;
   cp.init(lane, row_stride);
+  if (lane == 0) progress[wave] = 0;
+  int done = 0;
 
   // One piece: keys [k0, k1) of segment (b, hg), whose sequence starts at row
   // q0 and holds past + 1 keys.  nparts == 1: the piece is the whole segment.
@@ -655,6 +658,15 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt_le<(NS - 1) * 2 * SG::NI>();
       __builtin_amdgcn_sched_barrier(0);
+      // Waves w and w ^ 4 share a SIMD, whose issue arbitration favours the
+      // older wave: left alone, the younger one falls behind through every
+      // tile's computation, and the piece ends when its slowest wave does.
+      // A wave behind its partner in tiles computed raises its priority.
+      if constexpr (NW == 8) {
+        const int other = __builtin_amdgcn_readfirstlane(progress[wave ^ 4]);
+        if (done < other) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       uint8_t* slotp = myring + cur * SG::SLOT;
       TileRaw<KVF, D> t[HW];
 #pragma unroll
@@ -670,8 +682,11 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
 #pragma unroll
       for (int hh = 0; hh < HW; ++hh)
         compute_tile<KVF, D>(t[hh], k, ke, c2[hh], qhi[hh], qlo[hh], st[hh], grp);
+      ++done;
+      if (lane == 0) progress[wave] = done;
       cur = (cur + 1 == NS) ? 0 : cur + 1;
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt_le<0>();
     __builtin_amdgcn_sched_barrier(0);
 

@@ -141,8 +141,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // streaming at least kStreamMinTiles 32-key tiles (two per wave).
 constexpr int kStreamMinTiles = 16;
 
+// lengths_exact: the device lengths equal the host ones (false for the
+// block-sparse decode, whose host lengths are upper bounds): the
+// length-balanced partitions cut the tiles by the host lengths and need them
+// exact, so without it only the single pass and the chunk partition (cut on
+// the device) are planned.
 int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* past_host,
-                int num_splits, int num_cus, paq_plan* p) {
+                int num_splits, int num_cus, paq_plan* p, bool lengths_exact = true) {
   memset(p, 0, sizeof *p);
   SeqStats st;
   int rc = validate(d, cum_q_host, past_host, &st);
@@ -229,6 +234,10 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
     mode = paq::DEC_CHUNKS;
     S = num_splits;
   } else if (num_splits < 0) {
+    if (!lengths_exact)
+      return fail(PAQ_ERR_UNSUPPORTED,
+                  "a length-balanced partition needs exact key counts (block-sparse decode: "
+                  "num_splits >= 0)");
     if (!counters_fit)
       return fail(PAQ_ERR_UNSUPPORTED, "split decode of %d sequences x %d head groups: at most %d",
                   d->batch, hg, paq::kDecCounters);
@@ -248,7 +257,8 @@ int plan_decode(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
     for (int b = 0; b < d->batch; ++b)
       if (cum_q_host[b + 1] > cum_q_host[b]) sum_kv += (long)past_host[b] + 1;
     // (max > 1.5 x mean, and long enough for a split to pay: 512 keys)
-    const bool skewed = 2L * st.max_kv * st.active > 3L * sum_kv && st.max_kv >= 512;
+    const bool skewed =
+        lengths_exact && 2L * st.max_kv * st.active > 3L * sum_kv && st.max_kv >= 512;
     if (skewed) {
       groups = std::min<long>(std::min<long>(cus, paq::kDecMaxPartsPerSeq),
                               std::max<long>(1, total / kStreamMinTiles));
@@ -454,7 +464,7 @@ int plan_sparse(const paq_desc* d, const int32_t* cum_q_host, const int32_t* pas
                   n, max_sel, nb);
     (*past_c)[b] = n * d->block_size - 1;
   }
-  return plan_decode(dc, cum_q_host, past_c->data(), num_splits, 0, p);
+  return plan_decode(dc, cum_q_host, past_c->data(), num_splits, 0, p, false);
 }
 
 size_t sparse_head_bytes(int batch, int max_sel) {

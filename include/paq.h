@@ -296,8 +296,10 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
  *                with a new row (checked on the host)
  * Runs a small kernel that turns the selection into a compact block table
  * and effective key counts, then the dense decode kernels over it (single
- * pass or split-KV with num_splits as for paged_attn_decode, planned on
- * num_sel_host * block_size keys).  `workspace` (device, 16-byte aligned)
+ * pass or split-KV with num_splits >= 0 as for paged_attn_decode, planned on
+ * num_sel_host * block_size keys; the length-balanced partitions need exact
+ * key counts, so num_splits < 0 returns PAQ_ERR_UNSUPPORTED and the automatic
+ * choice never takes them).  `workspace` (device, 16-byte aligned)
  * must hold paged_attn_decode_sparse_workspace_size() bytes: the compact
  * table at its head is overwritten, and the rest is a paged_attn_decode
  * workspace with the same rule (arrival counters zero when a split call

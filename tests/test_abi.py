@@ -314,6 +314,28 @@ def test_sparse_decode_checks():
     rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, 1, FAKE, 16, None)
     assert rc == paq.PAQ_ERR_WORKSPACE
+    # the host key counts of a sparse call are upper bounds (the device knows
+    # the exact ones), so the length-balanced partition, which cuts tiles by
+    # the host counts, is refused; the automatic choice never takes it
+    rc = L.paged_attn_decode_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, pa, pb, FAKE, FAKE, pc, 3, 0.0, -4, FAKE, 1 << 20,
+                                    None)
+    assert rc == paq.PAQ_ERR_UNSUPPORTED and "exact key counts" in paq.paq_last_error()
+    assert paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [2, 1], 3, -4) == 0
+
+
+def test_sparse_decode_automatic_never_balanced():
+    """A skewed batch under-filling the device: the dense decode plans the
+    length-balanced partition, the sparse decode over the same lengths a
+    chunk partition."""
+    d = _desc(6, 6, nb=2000, mb=200)
+    cum = list(range(7))
+    past = [3000, 600, 700, 650, 800, 620]
+    p = paq.paq_plan_decode(d, cum, past, 0)
+    assert paq.PATHS[p.path] == "balanced"
+    ws = paq.paged_attn_decode_sparse_workspace_size(d, cum, past, [188, 38, 44, 41, 50, 39],
+                                                     188, 0)
+    assert ws > 0
 
 
 def test_sparse_prefill_checks():
