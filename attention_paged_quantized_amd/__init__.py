@@ -33,7 +33,8 @@ EXPORTS = ("paq_abi_version", "paq_status_string", "paq_last_error", "paq_plan_d
            "paged_attn_decode_host", "paged_attn_decode_sparse",
            "paged_attn_decode_sparse_workspace_size", "paged_attn_prefill_padded",
            "paged_attn_decode_noalloc", "paged_attn_prefill_sparse",
-           "paged_attn_prefill_sparse_workspace_size", "paged_attn_prefill_k_per_use")
+           "paged_attn_prefill_sparse_workspace_size", "paged_attn_prefill_k_per_use",
+           "paged_attn_decode_append")
 
 
 class PaqDesc(ctypes.Structure):
@@ -97,6 +98,10 @@ def lib():
         L.kv_quant_append.restype = ctypes.c_int32
         L.kv_quant_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP, _VP, _VP,
                                       _VP, _VP, _VP, _VP, _VP, _VP, _I32P, _I32P, _VP]
+        L.paged_attn_decode_append.restype = ctypes.c_int32
+        L.paged_attn_decode_append.argtypes = [ctypes.POINTER(PaqDesc), ctypes.c_int32, _VP,
+                                               _VP] + attn[1:] + [ctypes.c_int32, _VP,
+                                                                  ctypes.c_size_t, _VP]
         L.paged_attn_decode_sparse.restype = ctypes.c_int32
         L.paged_attn_decode_sparse.argtypes = attn[:-1] + [_VP, _VP, _I32P, ctypes.c_int32,
                                                            ctypes.c_float, ctypes.c_int32, _VP,
@@ -223,6 +228,24 @@ def paged_attn_decode(desc, query, out, key_cache, value_cache, k_scale, v_scale
         ctypes.byref(desc), _dev(query), _dev(out), _dev(key_cache), _dev(value_cache),
         _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q), _dev(past_lens), pa, pb,
         float(softmax_scale), int(num_splits), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_append(desc, kv_in_dtype, key, value, query, out, key_cache, value_cache,
+                             k_scale, v_scale, block_table, cum_q, past_lens, cum_q_host,
+                             past_lens_host, softmax_scale=0.0, num_splits=0, workspace=None,
+                             stream=None):
+    """kv_quant_append of the step's new key/value rows followed by
+    paged_attn_decode, in one call (the decode kernel appends the rows itself
+    where it can).  Same workspace rule as paged_attn_decode."""
+    a, pa = _host_i32(cum_q_host)
+    b, pb = _host_i32(past_lens_host)
+    dt = DTYPES[kv_in_dtype] if isinstance(kv_in_dtype, str) else int(kv_in_dtype)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attn_decode_append(
+        ctypes.byref(desc), dt, _dev(key), _dev(value), _dev(query), _dev(out), _dev(key_cache),
+        _dev(value_cache), _dev(k_scale), _dev(v_scale), _dev(block_table), _dev(cum_q),
+        _dev(past_lens), pa, pb, float(softmax_scale), int(num_splits), _dev(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def paged_attn_decode_noalloc(desc, query, out, key_cache, value_cache, k_scale, v_scale,

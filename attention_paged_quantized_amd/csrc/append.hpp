@@ -40,10 +40,10 @@ __device__ __forceinline__ void load_scales8(const float* __restrict__ sc, int h
   }
 }
 
-// codes of x / s for channels d0..d0+7 into the cache row `row` (C bytes)
+// The code bytes of x / s for 8 consecutive channels, as stored: 8 bytes
+// (INT8, FP8) or 4 (INT4, channel 2j in the low nibble); INT4 uses w[0] only.
 template <int KVF>
-__device__ __forceinline__ void store_codes8(uint8_t* row, int d0, const float (&x)[8],
-                                             const float (&s)[8]) {
+__device__ __forceinline__ u32x2 codes8(const float (&x)[8], const float (&s)[8]) {
   if constexpr (KVF == KV_INT8) {
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -51,13 +51,13 @@ __device__ __forceinline__ void store_codes8(uint8_t* row, int d0, const float (
       w0 |= (uint32_t)(quant_int(x[i] / s[i], 127.0f) & 0xFF) << (8 * i);
       w1 |= (uint32_t)(quant_int(x[4 + i] / s[4 + i], 127.0f) & 0xFF) << (8 * i);
     }
-    *reinterpret_cast<u32x2*>(row + d0) = (u32x2){w0, w1};
+    return (u32x2){w0, w1};
   } else if constexpr (KVF == KV_INT4) {
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       w |= (uint32_t)(quant_int(x[i] / s[i], 7.0f) & 0xF) << (4 * i);
-    *reinterpret_cast<uint32_t*>(row + d0 / 2) = w;
+    return (u32x2){w, 0u};
   } else {
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -65,8 +65,49 @@ __device__ __forceinline__ void store_codes8(uint8_t* row, int d0, const float (
       w0 |= e4m3_encode(x[i] / s[i]) << (8 * i);
       w1 |= e4m3_encode(x[4 + i] / s[4 + i]) << (8 * i);
     }
-    *reinterpret_cast<u32x2*>(row + d0) = (u32x2){w0, w1};
+    return (u32x2){w0, w1};
   }
+}
+
+// codes of x / s for channels d0..d0+7 into the cache row `row` (C bytes)
+template <int KVF>
+__device__ __forceinline__ void store_codes8(uint8_t* row, int d0, const float (&x)[8],
+                                             const float (&s)[8]) {
+  const u32x2 w = codes8<KVF>(x, s);
+  if constexpr (KVF == KV_INT4) *reinterpret_cast<uint32_t*>(row + d0 / 2) = w[0];
+  else *reinterpret_cast<u32x2*>(row + d0) = w;
+}
+
+// The 16 code bytes [bo, bo + 16) of the cache row of kv head h for the
+// input row x (head_size elements of kv head h), scales sc (per channel or
+// per head): channels bo.. (INT8, FP8) or 2 bo.. (INT4).  Same arithmetic as
+// store_codes8.
+template <int KVF, int SM, typename TI>
+__device__ __forceinline__ u32x4 codes16(const TI* __restrict__ x_row, const float* __restrict__ sc,
+                                         int h, int head_size, int bo) {
+  u32x4 r;
+  if constexpr (KVF == KV_INT4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d0 = 2 * bo + 8 * q;
+      float x[8], s[8];
+      load8(x_row + d0, x);
+      load_scales8<SM>(sc, h, head_size, d0, s);
+      r[q] = codes8<KVF>(x, s)[0];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int d0 = bo + 8 * q;
+      float x[8], s[8];
+      load8(x_row + d0, x);
+      load_scales8<SM>(sc, h, head_size, d0, s);
+      const u32x2 w = codes8<KVF>(x, s);
+      r[2 * q] = w[0];
+      r[2 * q + 1] = w[1];
+    }
+  }
+  return r;
 }
 
 // the cache row of position t of sequence b, kv head h

@@ -65,6 +65,12 @@ struct AttnArgs {
   int dec_chunks_per_part; // DEC_CHUNKS: consecutive chunks per part
   long long dec_total_tiles;  // DEC_STREAM: 32-key tiles of all segments
   float softmax_scale;  // already resolved (> 0)
+  // Decode with the step's append fused in (MFMA decode only): the new key
+  // and value rows (token_count, kv_num_heads, head_size) in the query's
+  // dtype, quantized into the caches by the wave that streams the tile
+  // holding them; null for a plain decode.
+  const void* new_key;
+  const void* new_value;
 };
 
 // Launch geometry shared by the host planner and the launchers.

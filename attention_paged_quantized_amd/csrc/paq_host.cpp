@@ -827,6 +827,54 @@ int32_t kv_quant_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
   return launched(paq::launch_quant_append(a, (hipStream_t)stream), "kv_quant_append");
 }
 
+int32_t paged_attn_decode_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
+                                 const void* value, const void* query, void* out,
+                                 void* key_cache, void* value_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* cum_q, const int32_t* past_lens,
+                                 const int32_t* cum_q_host, const int32_t* past_lens_host,
+                                 float softmax_scale, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  // Every check of both operations runs before anything is launched.
+  paq_plan p;
+  int rc = plan_decode(d, cum_q_host, past_lens_host, num_splits, 0, &p);
+  if (rc) return rc;
+  if (kv_in_dtype < PAQ_DT_F32 || kv_in_dtype > PAQ_DT_BF16)
+    return fail(PAQ_ERR_INVALID_ARG, "kv_in_dtype %d unknown", kv_in_dtype);
+  if (p.path == PAQ_PATH_NONE) return PAQ_OK;             // no new token: nothing to append
+  rc = check_attn_pointers(query, out, key_cache, value_cache, k_scale, v_scale, block_table,
+                           cum_q, past_lens);
+  if (rc) return rc;
+  if (!key || !value) return fail(PAQ_ERR_INVALID_ARG, "key / value is NULL");
+  if (p.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+      return fail(PAQ_ERR_WORKSPACE, "split decode needs %llu workspace bytes, got %llu",
+                  (unsigned long long)p.workspace_bytes, (unsigned long long)workspace_bytes);
+    if (((uintptr_t)workspace) % 16)
+      return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  // The MFMA decode quantizes the new rows itself (16-byte code stores and
+  // loads of the new rows in the query's dtype); anything else is the two
+  // operations one after the other on the stream.
+  const bool mfma = p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT ||
+                    p.path == PAQ_PATH_BALANCED;
+  const bool aligned = ((uintptr_t)key_cache | (uintptr_t)value_cache) % 16 == 0 &&
+                       ((uintptr_t)key | (uintptr_t)value) % 16 == 0;
+  if (!mfma || kv_in_dtype != d->q_dtype || !aligned) {
+    rc = kv_quant_append(d, kv_in_dtype, key, value, key_cache, value_cache, k_scale, v_scale,
+                         block_table, cum_q, past_lens, cum_q_host, past_lens_host, stream);
+    if (rc) return rc;
+    return paq::decode_entry(d, query, out, key_cache, value_cache, k_scale, v_scale,
+                             block_table, cum_q, past_lens, cum_q_host, past_lens_host,
+                             softmax_scale, num_splits, workspace, workspace_bytes, stream);
+  }
+  paq::AttnArgs a = attn_args(d, query, out, key_cache, value_cache, k_scale, v_scale,
+                              block_table, cum_q, past_lens, softmax_scale, p);
+  a.new_key = key;
+  a.new_value = value;
+  return run_decode(d, p, a, workspace, (hipStream_t)stream);
+}
+
 int32_t paged_attn_decode_host(const paq_desc* d, const float* query, float* out,
                                const void* key_cache, const void* value_cache,
                                const float* k_scale, const float* v_scale,

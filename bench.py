@@ -88,6 +88,9 @@ def parse():
                     help="prefill: K codes kept raw in LDS and converted by every wave at "
                          "each use (paged_attn_prefill_k_per_use), the staging scheme the "
                          "default is compared with")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode: the step as kv_quant_append then paged_attn_decode (two "
+                         "calls) instead of one paged_attn_decode_append call")
     ap.add_argument("--only", action="store_true",
                     help="measure the --workload alone (no configs / ablations)")
     return ap.parse_args()
@@ -510,10 +513,13 @@ _WORKLOADS = {}          # workloads built so far (the ablations reuse them)
 
 
 def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, warm=True,
-            append_loop=True, k_per_use=False):
+            append_loop=True, k_per_use=False, separate=False):
     """Time `steps` steps (append + attention) of workload `name` after
     `warmup` untimed ones; returns the measurement as a dict, plus the
-    workload, one filled Device and the descriptor (for the CPU figures)."""
+    workload, one filled Device and the descriptor (for the CPU figures).
+    A dense decode step is one paged_attn_decode_append call (the decode
+    kernel appends the step's rows itself where it can); separate=True runs
+    kv_quant_append and paged_attn_decode instead."""
     import torch
     import attention_paged_quantized_amd as paq
     import workloads
@@ -565,8 +571,14 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                                                              sel_np.shape[1], S)
         ws = torch.zeros(nbytes // 4 + 1, dtype=torch.float32, device=dev)
 
+    fused = kind == "decode" and not sparse and not rotary and not separate
+
     def attention(g, out):
-        if kind == "decode" and sparse:
+        if fused:
+            paq.paged_attn_decode_append(desc, w.kv_in_dtype, kin, vin, g.query, out, g.kc, g.vc,
+                                         g.k_scale, g.v_scale, g.block_table, g.cum_q, g.past,
+                                         w.cum_q, w.past_lens, 0.0, S, ws, stream)
+        elif kind == "decode" and sparse:
             paq.paged_attn_decode_sparse(desc, g.query, out, g.kc, g.vc, g.k_scale, g.v_scale,
                                          g.block_table, g.cum_q, g.past, w.cum_q, w.past_lens,
                                          sel_d, num_d, num_np, 0.0, S, ws, stream)
@@ -604,7 +616,8 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
 
     def step(i, ev=None):
         g = devs[i % pools]
-        append(g)
+        if not fused:
+            append(g)
         if ev is not None:
             ev[0].record(stream)
         attention(g, outs[i % pools])
@@ -722,7 +735,13 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                          "kernel": ("paged_attn_decode_sparse call (sparse_compact_kernel + %s)"
-                                    if sparse else "paged_attn_decode call (%s)") % call,
+                                    if sparse else
+                                    "paged_attn_decode_append call (%s%s)" % (
+                                        "%s", ", the step's append inside"
+                                        if call == "decode_stream_kernel" and
+                                        w.kv_in_dtype == w.q_dtype else
+                                        " after quant_append_kernel")
+                                    if fused else "paged_attn_decode call (%s)") % call,
                          "kernel_us_avg": round(kern_avg * 1e3, 3),
                          "per_call_events_us_p10_p90": p10p90,
                          "warm_cache_us": round(warm_ms * 1e3, 3) if warm_ms else None,
@@ -810,7 +829,8 @@ def main():
     torch.cuda.set_device(0)
     paq.lib()
     r, w, g0, desc = measure(args, args.workload, splits=args.splits, padded=args.padded_grid,
-                             rotary=args.rotary, sparse=args.sparse, k_per_use=args.k_per_use)
+                             rotary=args.rotary, sparse=args.sparse, k_per_use=args.k_per_use,
+                             separate=args.separate)
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16"}.get(w.q_dtype, "f16"),
@@ -839,7 +859,8 @@ def main():
         torch.cuda.synchronize()
     del src, dst
 
-    if not args.only and not args.sparse and not args.rotary and not args.k_per_use:
+    if not args.only and not args.sparse and not args.rotary and not args.k_per_use and \
+            not args.separate:
         # every configuration, then the ablations (short timings each)
         configs = {}
         for name in ("tiny_decode", "int8_decode", "int4_long", "int8_prefill", "fp8_prefill"):
@@ -862,11 +883,14 @@ def main():
                 ("int8_decode block-sparse (2-block window + every 3rd block)", "int8_decode",
                  {"sparse": True}),
                 ("int8_prefill block-sparse (local blocks + 2 before + every 3rd)",
-                 "int8_prefill", {"sparse": True})):
+                 "int8_prefill", {"sparse": True}),
+                ("int8_decode step as two calls (kv_quant_append, then paged_attn_decode)",
+                 "int8_decode", {"separate": True})):
             ar = measure(args, name, warm=False, append_loop=False, **kw)[0]
             s = summary(ar)
             ref = configs[name]
             s["time_vs_default"] = round(s["kernel_us_avg"] / ref["kernel_us_avg"], 3)
+            s["step_vs_default"] = round(s["ms_per_step"] / ref["ms_per_step"], 3)
             abl[label] = s
         result["ablations"] = abl
 

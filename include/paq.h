@@ -218,6 +218,30 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* One decode step in one call: kv_quant_append of the step's new key and
+ * value rows (key, value: (token_count, kv_num_heads, head_size) in
+ * kv_in_dtype, device) followed by paged_attn_decode, with the same results
+ * (cache bytes identical to kv_quant_append's, outputs identical to
+ * paged_attn_decode's over the appended cache).  The append of the step is
+ * the first half of the pages' decode step ("ONNX Runtime: INT4 Paged KV
+ * Cache", sections 2-3: the new token's codes are written into its slot
+ * before attention reads the cache).  When the call takes the MFMA decode,
+ * kv_in_dtype equals q_dtype and key, value and both caches are 16-byte
+ * aligned, the decode kernel quantizes and stores the new rows itself -- the
+ * wave that streams the tile holding the new token also places its codes in
+ * that tile -- so the step is one launch; otherwise the two operations run
+ * one after the other on `stream`.  Arguments, workspace rule and errors as
+ * for kv_quant_append and paged_attn_decode; all checks of both run before
+ * anything is launched. */
+int32_t paged_attn_decode_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,
+                                 const void* value, const void* query, void* out,
+                                 void* key_cache, void* value_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* cum_q, const int32_t* past_lens,
+                                 const int32_t* cum_q_host, const int32_t* past_lens_host,
+                                 float softmax_scale, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* paged_attn_decode without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The workspace of split and

@@ -265,6 +265,31 @@ def test_decode_specific_checks():
     assert _call_decode(_desc(1, 1), [0, 1], [4], ptr=None) == paq.PAQ_ERR_INVALID_ARG
 
 
+def _call_decode_append(d, cum, past, kv_in=1, key=FAKE, splits=1, ws=None, ws_bytes=0):
+    L = paq.lib()
+    a, pa = paq._host_i32(cum)
+    b, pb = paq._host_i32(past)
+    return L.paged_attn_decode_append(ctypes.byref(d), kv_in, key, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, pa, pb, 0.0, splits, ws,
+                                      ws_bytes, None)
+
+
+def test_decode_append_checks():
+    """The fused decode step refuses what either of its operations refuses,
+    before anything is launched."""
+    d = _desc(2, 3)
+    assert _call_decode_append(d, [0, 2, 3], [4, 4]) == paq.PAQ_ERR_INVALID_ARG   # q_len 2
+    d = _desc(1, 1)
+    assert _call_decode_append(d, [0, 1], [4], kv_in=9) == paq.PAQ_ERR_INVALID_ARG
+    assert "kv_in_dtype" in paq.paq_last_error()
+    assert _call_decode_append(d, [0, 1], [4], key=None) == paq.PAQ_ERR_INVALID_ARG
+    assert _call_decode_append(d, [0, 1], [100], splits=4) == paq.PAQ_ERR_WORKSPACE
+    assert _call_decode_append(d, [0, 1], [100], splits=4, ws=FAKE, ws_bytes=64) == \
+        paq.PAQ_ERR_WORKSPACE
+    # no new token: nothing to append or attend, NULL rows accepted
+    assert _call_decode_append(_desc(1, 0), [0, 0], [4], key=None) == paq.PAQ_OK
+
+
 def test_bad_enums_and_null_host_arrays():
     assert _call_decode(_desc(1, 1, q="f16", fmt=7), [0, 1], [0]) == paq.PAQ_ERR_INVALID_ARG
     assert _call_decode(_desc(1, 1, mode=5), [0, 1], [0]) == paq.PAQ_ERR_INVALID_ARG
