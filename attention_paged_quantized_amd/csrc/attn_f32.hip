@@ -16,6 +16,7 @@
 // times key scale over its power-of-two normaliser, dotted with the codes);
 // exponents are formed as (raw - raw max) * factor, so key scales anywhere in
 // the finite fp32 range neither overflow nor produce a NaN.
+#include "append.hpp"
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -69,7 +70,13 @@ __device__ __forceinline__ float code_at(const uint8_t* row, int d) {
 
 // MG: the largest GQA group the instance serves (4 or 16): loops over the
 // group and the LDS arrays are sized by it, so small groups run short code.
-template <int KVF, int SM, typename TQ, int MG>
+// APPEND: the decode step's new key and value rows (a.new_key / a.new_value,
+// in the query's dtype) are quantized here by the workgroup whose chunk holds
+// the new key -- threads [0, 2 D / 8) form 8 channels' codes each with the
+// append's arithmetic, store them into the caches and into LDS -- and the
+// thread of that key takes its codes from LDS, so the cache store needs no
+// wait.
+template <int KVF, int SM, typename TQ, int MG, bool APPEND>
 __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   const int r = blockIdx.x;
   const int g = blockIdx.y;
@@ -96,6 +103,21 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
       const int hh = i / D, d = i % D;
       qv[u] = to_f32(q[((size_t)r * H + g * G + hh) * D + d]);
       sv[u] = (SM == SCALE_CHANNEL) ? a.k_scale[g * D + d] : a.k_scale[g];
+    }
+  }
+
+  // the new rows' elements of this thread's 8 channels (loads go out now)
+  const int app_units = 2 * D / 8;                      // 8-channel groups of K and V
+  const bool app_thread = APPEND && tid < app_units;
+  const bool app_v = tid >= D / 8;
+  const int app_d0 = 8 * (app_v ? tid - D / 8 : tid);
+  float app_x[8], app_s[8];
+  if constexpr (APPEND) {
+    if (app_thread) {
+      load8(reinterpret_cast<const TQ*>(app_v ? a.new_value : a.new_key) +
+                ((size_t)r * hkv + g) * D + app_d0,
+            app_x);
+      load_scales8<SM>(app_v ? a.v_scale : a.k_scale, g, D, app_d0, app_s);
     }
   }
 
@@ -126,6 +148,27 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   __shared__ float m_sh[MG], l_sh[MG], alpha_sh[MG];
   __shared__ int e_sh;
   __shared__ __attribute__((aligned(16))) uint8_t vrows[kF32Threads * (kF32MaxD + 16)];
+  __shared__ __attribute__((aligned(16))) uint8_t new_rows[2][kF32MaxD];   // fused append
+
+  // fused append: this chunk holds the new key (decode: row r is the
+  // sequence's one new token, at key `past`)
+  const bool app_here = APPEND && qlen == 1 && kbeg <= past && past < kend;
+  if constexpr (APPEND) {
+    if (app_here && app_thread) {
+      const u32x2 w = codes8<KVF>(app_x, app_s);
+      const int ob = (KVF == KV_INT4) ? app_d0 / 2 : app_d0;   // byte offset in the row
+      const int blk = table[past / bs];
+      uint8_t* dst = const_cast<uint8_t*>(app_v ? a.value_cache : a.key_cache) +
+                     (((size_t)blk * bs + past % bs) * hkv + g) * C + ob;
+      if constexpr (KVF == KV_INT4) {
+        *reinterpret_cast<uint32_t*>(dst) = w[0];
+        *reinterpret_cast<uint32_t*>(&new_rows[app_v][ob]) = w[0];
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = w;
+        *reinterpret_cast<u32x2*>(&new_rows[app_v][ob]) = w;
+      }
+    }
+  }
 
   // q' = q * s / M with M = 2^e >= max|s| of this kv head (exact scaling; M
   // finite for every finite scale): raw scores q'.codes never overflow, and
@@ -156,14 +199,24 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int hh = 0; hh < MG; ++hh) dot[hh] = 0.f;
     if (j < kend) {
-      const int blk = table[j / bs];
-      const size_t off = (((size_t)blk * bs + j % bs) * hkv + g) * C;
       u32x4 kw[kF32Units], vw[kF32Units];
+      if (APPEND && app_here && j == past) {
+        // the new key's codes, formed above (the cache store may not have landed)
 #pragma unroll
-      for (int u = 0; u < kF32Units; ++u) {
-        if (16 * u >= C) break;
-        kw[u] = *reinterpret_cast<const u32x4*>(a.key_cache + off + 16 * u);
-        vw[u] = *reinterpret_cast<const u32x4*>(a.value_cache + off + 16 * u);
+        for (int u = 0; u < kF32Units; ++u) {
+          if (16 * u >= C) break;
+          kw[u] = *reinterpret_cast<const u32x4*>(&new_rows[0][16 * u]);
+          vw[u] = *reinterpret_cast<const u32x4*>(&new_rows[1][16 * u]);
+        }
+      } else {
+        const int blk = table[j / bs];
+        const size_t off = (((size_t)blk * bs + j % bs) * hkv + g) * C;
+#pragma unroll
+        for (int u = 0; u < kF32Units; ++u) {
+          if (16 * u >= C) break;
+          kw[u] = *reinterpret_cast<const u32x4*>(a.key_cache + off + 16 * u);
+          vw[u] = *reinterpret_cast<const u32x4*>(a.value_cache + off + 16 * u);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kF32Units; ++u) {
@@ -292,14 +345,20 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int KVF, int SM, int MG>
-static int launch_q(const AttnArgs& a, dim3 grid, hipStream_t st) {
+template <int KVF, int SM, int MG, bool APPEND>
+static int launch_qa(const AttnArgs& a, dim3 grid, hipStream_t st) {
   switch (a.q_dtype) {
-    case DT_F32: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, float, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
-    case DT_F16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, f16, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
-    case DT_BF16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, bf16, MG>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_F32: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, float, MG, APPEND>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_F16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, f16, MG, APPEND>), grid, dim3(kF32Threads), 0, st, a); return 0;
+    case DT_BF16: hipLaunchKernelGGL((attn_f32_kernel<KVF, SM, bf16, MG, APPEND>), grid, dim3(kF32Threads), 0, st, a); return 0;
   }
   return -1;
+}
+
+template <int KVF, int SM, int MG>
+static int launch_q(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  return a.new_key ? launch_qa<KVF, SM, MG, true>(a, grid, st)
+                   : launch_qa<KVF, SM, MG, false>(a, grid, st);
 }
 
 template <int KVF, int SM>

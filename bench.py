@@ -738,8 +738,7 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                                     if sparse else
                                     "paged_attn_decode_append call (%s%s)" % (
                                         "%s", ", the step's append inside"
-                                        if call == "decode_stream_kernel" and
-                                        w.kv_in_dtype == w.q_dtype else
+                                        if w.kv_in_dtype == w.q_dtype else
                                         " after quant_append_kernel")
                                     if fused else "paged_attn_decode call (%s)") % call,
                          "kernel_us_avg": round(kern_avg * 1e3, 3),

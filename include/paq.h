@@ -225,12 +225,13 @@ int32_t paged_attn_decode(const paq_desc* d, const void* query, void* out,
  * paged_attn_decode's over the appended cache).  The append of the step is
  * the first half of the pages' decode step ("ONNX Runtime: INT4 Paged KV
  * Cache", sections 2-3: the new token's codes are written into its slot
- * before attention reads the cache).  When the call takes the MFMA decode,
- * kv_in_dtype equals q_dtype and key, value and both caches are 16-byte
- * aligned, the decode kernel quantizes and stores the new rows itself -- the
- * wave that streams the tile holding the new token also places its codes in
- * that tile -- so the step is one launch; otherwise the two operations run
- * one after the other on `stream`.  Arguments, workspace rule and errors as
+ * before attention reads the cache).  When kv_in_dtype equals q_dtype and
+ * key, value and both caches are 16-byte aligned, the decode kernel (MFMA or
+ * fp32) quantizes and stores the new rows itself -- the wave or thread that
+ * reads the new token's key takes its codes from where they were formed, not
+ * from the cache -- so the step is one launch (two with the fp32 kernel's
+ * split-KV combine); otherwise the two operations run one after the other on
+ * `stream`.  Arguments, workspace rule and errors as
  * for kv_quant_append and paged_attn_decode; all checks of both run before
  * anything is launched. */
 int32_t paged_attn_decode_append(const paq_desc* d, int32_t kv_in_dtype, const void* key,

@@ -11,8 +11,10 @@ holding the new token's tile places its codes in the tile), and both match
 the oracle.  The cases cover the three formats, both scale modes, head sizes
 64 and 128 (one and two kv heads per wave), the single pass, block-aligned
 chunks and the balanced partition, sequences without a new token, new tokens
-at the first, middle and last row of a tile, and the paths that run the two
-operations separately (fp32 queries, key rows in another dtype).
+at the first, middle and last row of a tile, the fp32 kernel's own fused
+append (fp32 queries, groups beyond the MFMA decode's), the path that runs the
+two operations separately (key rows in another dtype), and the whole
+tiny_decode and int8_decode steps.
 """
 
 import itertools
@@ -88,17 +90,44 @@ def test_decode_append_matches_two_calls(fmt, D, mode, splits):
     _both(w, splits)
 
 
-@pytest.mark.parametrize("q_dtype,kv_in", [("f32", "f32"), ("f16", "f32")])
-def test_decode_append_two_launch_paths(q_dtype, kv_in):
-    """fp32 queries (the fp32 kernel) and key rows in another dtype than the
-    query's take the two operations one after the other: same results."""
-    name = "dapp_sep_%s_%s" % (q_dtype, kv_in)
+@pytest.mark.parametrize("fmt,D,mode,splits", list(itertools.product(
+    FORMATS, [64, 128], ["channel", "head"], [1, 3])))
+def test_decode_append_fp32_kernel(fmt, D, mode, splits):
+    """fp32 queries take the fp32 kernel, which appends the new rows itself
+    too (single pass, and split-KV with its combine)."""
+    name = "dapp_f32_%s_d%d_%s_s%d" % (fmt, D, mode, splits)
     print("case", name, flush=True)
-    w = workloads.custom(name, 3101 + len(q_dtype), batch=3, num_heads=8, kv_num_heads=2,
-                         head_size=128, block_size=16, past=np.array([40, 0, 300]),
-                         q_lens=np.ones(3, np.int32), q_dtype=q_dtype, kv_format="int8",
-                         kv_in_dtype=kv_in, num_splits=1)
+    w = workloads.custom(name, 3101 + 5 * FORMATS.index(fmt) + D + splits, batch=4, num_heads=8,
+                         kv_num_heads=2, head_size=D, block_size=16,
+                         past=np.array([40, 0, 300, 17]), q_lens=np.array([1, 1, 1, 0]),
+                         q_dtype="f32", kv_format=fmt, scale_mode=mode, num_splits=splits)
+    _both(w, splits)
+
+
+def test_decode_append_fp32_kernel_large_group():
+    """A 16-bit query with a GQA group of 12 takes the fp32 kernel (its
+    16-query-head instance) with the append inside."""
+    w = workloads.custom("dapp_g12", 3201, batch=3, num_heads=24, kv_num_heads=2,
+                         head_size=128, block_size=16, past=np.array([63, 64, 500]),
+                         q_lens=np.ones(3, np.int32), q_dtype="bf16", kv_format="int8",
+                         num_splits=1)
     _both(w, 1)
+
+
+def test_decode_append_two_launches():
+    """New rows in another dtype than the query's take the two operations one
+    after the other: same results."""
+    w = workloads.custom("dapp_sep", 3301, batch=3, num_heads=8, kv_num_heads=2,
+                         head_size=128, block_size=16, past=np.array([40, 0, 300]),
+                         q_lens=np.ones(3, np.int32), q_dtype="f16", kv_format="int8",
+                         kv_in_dtype="f32", num_splits=1)
+    _both(w, 1)
+
+
+def test_decode_append_tiny_decode():
+    """The tiny_decode step (fp32 queries, fp32 kernel)."""
+    w = workloads.make("tiny_decode")
+    _both(w, w.num_splits)
 
 
 def test_decode_append_full_int8_decode():
