@@ -78,36 +78,60 @@ __device__ __forceinline__ void store_codes8(uint8_t* row, int d0, const float (
   else *reinterpret_cast<u32x2*>(row + d0) = w;
 }
 
-// The 16 code bytes [bo, bo + 16) of the cache row of kv head h for the
-// input row x (head_size elements of kv head h), scales sc (per channel or
-// per head): channels bo.. (INT8, FP8) or 2 bo.. (INT4).  Same arithmetic as
-// store_codes8.
+// The 4 code bytes [bo, bo + 4) of a cache row (channels bo..bo+3 for INT8
+// and FP8, 2 bo..2 bo+7 for INT4) in two steps: the raw input elements and
+// scales behind them, then the codes (the arithmetic of store_codes8).
+struct Raw4 {
+  u32x4 x[2];    // up to 8 input elements (fp32: 32 bytes)
+  f32x4 s[2];    // their scales
+};
 template <int KVF, int SM, typename TI>
-__device__ __forceinline__ u32x4 codes16(const TI* __restrict__ x_row, const float* __restrict__ sc,
-                                         int h, int head_size, int bo) {
-  u32x4 r;
-  if constexpr (KVF == KV_INT4) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d0 = 2 * bo + 8 * q;
-      float x[8], s[8];
-      load8(x_row + d0, x);
-      load_scales8<SM>(sc, h, head_size, d0, s);
-      r[q] = codes8<KVF>(x, s)[0];
-    }
+__device__ __forceinline__ void load_raw4(const TI* __restrict__ x_row,
+                                          const float* __restrict__ sc, int h, int head_size,
+                                          int bo, Raw4& r) {
+  constexpr int N = KVF == KV_INT4 ? 8 : 4;                 // channels
+  const int d0 = KVF == KV_INT4 ? 2 * bo : bo;
+  const u32x4* xp = reinterpret_cast<const u32x4*>(x_row + d0);
+  if constexpr (N * sizeof(TI) == 32) {
+    r.x[0] = xp[0]; r.x[1] = xp[1];
+  } else if constexpr (N * sizeof(TI) == 16) {
+    r.x[0] = xp[0];
   } else {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int d0 = bo + 8 * q;
-      float x[8], s[8];
-      load8(x_row + d0, x);
-      load_scales8<SM>(sc, h, head_size, d0, s);
-      const u32x2 w = codes8<KVF>(x, s);
-      r[2 * q] = w[0];
-      r[2 * q + 1] = w[1];
-    }
+    const u32x2 v = *reinterpret_cast<const u32x2*>(x_row + d0);
+    r.x[0] = (u32x4){v[0], v[1], 0u, 0u};
   }
-  return r;
+  if constexpr (SM == SCALE_CHANNEL) {
+    const f32x4* sp = reinterpret_cast<const f32x4*>(sc + h * head_size + d0);
+    r.s[0] = sp[0];
+    if constexpr (N == 8) r.s[1] = sp[1];
+  } else {
+    const float v = sc[h];
+    r.s[0] = (f32x4){v, v, v, v};
+    r.s[1] = r.s[0];
+  }
+}
+template <int KVF, typename TI>
+__device__ __forceinline__ uint32_t codes4_from(const Raw4& r) {
+  constexpr int N = KVF == KV_INT4 ? 8 : 4;
+  const TI* e = reinterpret_cast<const TI*>(r.x);
+  float x[8], s[8];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i] = to_f32(e[i]);
+    s[i] = r.s[i / 4][i % 4];
+  }
+  if constexpr (KVF == KV_INT4) {
+    return codes8<KVF>(x, s)[0];
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = (KVF == KV_INT8) ? (uint32_t)(quant_int(x[i] / s[i], 127.0f) & 0xFF)
+                                          : e4m3_encode(x[i] / s[i]);
+      w |= c << (8 * i);
+    }
+    return w;
+  }
 }
 
 // the cache row of position t of sequence b, kv head h

@@ -35,6 +35,8 @@
 //   block-aligned chunks per sequence, or an equal share of all tiles per
 //   workgroup (see the partition below); partial results are merged by the
 //   last workgroup of a sequence to finish, inside the same launch.
+#include <type_traits>
+
 #include "append.hpp"
 #include "device.hpp"
 #include "launch.hpp"
@@ -577,7 +579,9 @@ __device__ __forceinline__ void chunk_part_keys(const AttnArgs& a, int j, int kv
 // pieces (stream) for one head group of HW adjacent kv heads; the NW waves
 // take the 32-key tiles of a piece in turn, each with its own online softmax,
 // and merge through LDS at the end of the piece.
-template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, int MODE, bool APPEND>
+// APPEND: 0 plain decode; 1 the step's new rows fused in, in the query's
+// dtype; 2 the same, new rows in fp32.
+template <int D, int KVF, int SM, typename TQ, int NW, int NS, int HW, int MODE, int APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     AttnArgs a, const int32_t* __restrict__ block_table) {
   using Geo = KvGeom<KVF, D>;
@@ -629,29 +633,36 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
       load_query<D, SM, TQ>(a, hg * HW + hh, q0, G, col, grp, qraw[hh]);
     // Fused append: the step's new token sits at key `past` (the last key).
     // The wave whose tile holds it quantizes the new key and value rows of
-    // its HW heads -- lanes [0, CH) 16 bytes of the key row segment each,
-    // lanes [CH, 2 CH) of the value row -- stores them into the caches, and
-    // writes the same bytes over that row of the tile (and the rows after
-    // it, copies of it) once the tile is in LDS (the copy may have read the
-    // slot before the store), so no wait on the store is needed.
+    // its HW heads -- lane l < RB / 4 forms 4 bytes of the key row segment,
+    // the next RB / 4 lanes 4 bytes of the value row, so no lane does more
+    // than 8 channels -- stores them into the caches, and writes the same
+    // bytes over that row of the tile (and the rows after it, copies of it)
+    // once the tile is in LDS (the copy may have read the slot before the
+    // store), so no wait on the store is needed.  (Forming the codes before
+    // the first copies measured faster than after them.)
     const int kt_app = k0 + 32 * ((past - k0) >> 5);       // tile holding the new key
     const bool app = APPEND && k0 <= past && past < k1 &&
                      (((past - k0) >> 5) % NW) == wave;
-    u32x4 app_codes = (u32x4){0u, 0u, 0u, 0u};
-    if constexpr (APPEND) {
-      if (app && lane < 2 * SG::CH) {
-        const bool is_v = lane >= SG::CH;
-        const int c = is_v ? lane - SG::CH : lane;
-        const int hh = (16 * c) / SG::C, bo = (16 * c) % SG::C;
+    constexpr int kAppLanes = SG::RB / 4;                  // lanes per row segment
+    const bool app_lane = app && lane < 2 * kAppLanes;
+    const bool app_v = lane >= kAppLanes;
+    const int app_b = 4 * (app_v ? lane - kAppLanes : lane);   // byte in the segment
+    uint32_t app_codes = 0;
+    if constexpr (APPEND != 0) {
+      if (app_lane) {
+        const int hh = app_b / SG::C, bo = app_b % SG::C;
         const int h = hg * HW + hh;
-        const TQ* x_row = reinterpret_cast<const TQ*>(is_v ? a.new_value : a.new_key) +
+        using TI = typename std::conditional<APPEND == 2, float, TQ>::type;
+        const TI* x_row = reinterpret_cast<const TI*>(app_v ? a.new_value : a.new_key) +
                           ((size_t)q0 * hkv + h) * D;
-        app_codes = codes16<KVF, SM, TQ>(x_row, is_v ? a.v_scale : a.k_scale, h, D, bo);
+        Raw4 raw;
+        load_raw4<KVF, SM, TI>(x_row, app_v ? a.v_scale : a.k_scale, h, D, bo, raw);
+        app_codes = codes4_from<KVF, TI>(raw);
         const int32_t blk = table[past >> lbs];
-        uint8_t* dst = const_cast<uint8_t*>(is_v ? a.value_cache : a.key_cache) +
+        uint8_t* dst = const_cast<uint8_t*>(app_v ? a.value_cache : a.key_cache) +
                        (((size_t)blk << lbs) + (size_t)(past & ((1 << lbs) - 1))) * row_stride +
-                       (size_t)hg * SG::RB + 16 * c;
-        *reinterpret_cast<u32x4*>(dst) = app_codes;
+                       (size_t)hg * SG::RB + app_b;
+        *reinterpret_cast<uint32_t*>(dst) = app_codes;
       }
     }
     if (kb < ke)
@@ -696,15 +707,14 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
         else __builtin_amdgcn_s_setprio(0);
       }
       uint8_t* slotp = myring + cur * SG::SLOT;
-      if constexpr (APPEND) {
+      if constexpr (APPEND != 0) {
         // the new key's row and the rows after it, which the copy fills with
         // the last key's row again (masked, but their value bytes still meet
         // a zero probability: a stale FP8 NaN there would survive it)
-        if (app && k == kt_app && lane < 2 * SG::CH) {
-          const int c = lane < SG::CH ? lane : lane - SG::CH;
-          uint8_t* half = slotp + (lane < SG::CH ? 0 : 32 * SG::RB);
+        if (app_lane && k == kt_app) {
+          uint8_t* half = slotp + (app_v ? 32 * SG::RB : 0);
           for (int r = past - kt_app; r < 32; ++r)
-            *reinterpret_cast<u32x4*>(half + stream_off<KVF, D, HW>(r, 16 * c)) = app_codes;
+            *reinterpret_cast<uint32_t*>(half + stream_off<KVF, D, HW>(r, app_b)) = app_codes;
         }
       }
       TileRaw<KVF, D> t[HW];
@@ -952,7 +962,7 @@ bool decode_mfma_supports(int head_size, int group, int block_size, int q_dtype)
 // then keep ~64 KB per CU in flight, where measured HBM efficiency peaks).
 // The partition, the part count and the waves per workgroup come from the
 // host plan.
-template <int D, int KVF, int SM, typename TQ, int HW, int NW, bool APPEND>
+template <int D, int KVF, int SM, typename TQ, int HW, int NW, int APPEND>
 static int launch_nw(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.grid_x), block(NW * 64);
   switch (a.dec_mode) {
@@ -975,8 +985,9 @@ static int launch_nw(const AttnArgs& a, hipStream_t st) {
 template <int D, int KVF, int SM, typename TQ, int HW>
 static int launch_hw_q(const AttnArgs& a, hipStream_t st) {
   if (a.dec_waves != 8) return -1;
-  if (a.new_key) return launch_nw<D, KVF, SM, TQ, HW, 8, true>(a, st);
-  return launch_nw<D, KVF, SM, TQ, HW, 8, false>(a, st);
+  if (a.new_key && a.new_rows_f32) return launch_nw<D, KVF, SM, TQ, HW, 8, 2>(a, st);
+  if (a.new_key) return launch_nw<D, KVF, SM, TQ, HW, 8, 1>(a, st);
+  return launch_nw<D, KVF, SM, TQ, HW, 8, 0>(a, st);
 }
 
 template <int D, int KVF, int SM, int HW>

@@ -71,6 +71,7 @@ struct AttnArgs {
   // holding them; null for a plain decode.
   const void* new_key;
   const void* new_value;
+  int new_rows_f32;     // MFMA decode: the new rows are fp32 (else the query's dtype)
 };
 
 // Launch geometry shared by the host planner and the launchers.

@@ -853,13 +853,16 @@ int32_t paged_attn_decode_append(const paq_desc* d, int32_t kv_in_dtype, const v
     if (((uintptr_t)workspace) % 16)
       return fail(PAQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
-  // The decode kernels (MFMA and fp32) quantize the new rows themselves when
-  // the rows come in the query's dtype and everything is 16-byte aligned (16-
-  // byte code stores and row loads); otherwise the two operations run one
-  // after the other on the stream.
+  // The decode kernels quantize the new rows themselves when everything is
+  // 16-byte aligned (16-byte code stores and row loads) and the rows come in
+  // the query's dtype (or in fp32, for the MFMA decode); otherwise the two
+  // operations run one after the other on the stream.
   const bool aligned = ((uintptr_t)key_cache | (uintptr_t)value_cache) % 16 == 0 &&
                        ((uintptr_t)key | (uintptr_t)value) % 16 == 0;
-  if (kv_in_dtype != d->q_dtype || !aligned) {
+  const bool mfma = p.path == PAQ_PATH_SINGLE || p.path == PAQ_PATH_SPLIT ||
+                    p.path == PAQ_PATH_BALANCED;
+  const bool rows_ok = kv_in_dtype == d->q_dtype || (mfma && kv_in_dtype == PAQ_DT_F32);
+  if (!rows_ok || !aligned) {
     rc = kv_quant_append(d, kv_in_dtype, key, value, key_cache, value_cache, k_scale, v_scale,
                          block_table, cum_q, past_lens, cum_q_host, past_lens_host, stream);
     if (rc) return rc;
@@ -871,6 +874,7 @@ int32_t paged_attn_decode_append(const paq_desc* d, int32_t kv_in_dtype, const v
                               block_table, cum_q, past_lens, softmax_scale, p);
   a.new_key = key;
   a.new_value = value;
+  a.new_rows_f32 = kv_in_dtype == PAQ_DT_F32 && d->q_dtype != PAQ_DT_F32;
   return run_decode(d, p, a, workspace, (hipStream_t)stream);
 }
 

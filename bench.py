@@ -738,7 +738,9 @@ def measure(args, name, splits=None, padded=False, rotary=False, sparse=False, w
                                     if sparse else
                                     "paged_attn_decode_append call (%s%s)" % (
                                         "%s", ", the step's append inside"
-                                        if w.kv_in_dtype == w.q_dtype else
+                                        if w.kv_in_dtype == w.q_dtype or
+                                        (w.kv_in_dtype == "f32" and
+                                         call == "decode_stream_kernel") else
                                         " after quant_append_kernel")
                                     if fused else "paged_attn_decode call (%s)") % call,
                          "kernel_us_avg": round(kern_avg * 1e3, 3),

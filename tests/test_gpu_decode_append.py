@@ -114,14 +114,33 @@ def test_decode_append_fp32_kernel_large_group():
     _both(w, 1)
 
 
+@pytest.mark.parametrize("fmt,splits", list(itertools.product(FORMATS, [1, 6])))
+def test_decode_append_fp32_rows(fmt, splits):
+    """16-bit queries with fp32 new rows: the MFMA decode appends them itself."""
+    name = "dapp_rows32_%s_s%d" % (fmt, splits)
+    print("case", name, flush=True)
+    w = workloads.custom(name, 3301 + 3 * FORMATS.index(fmt) + splits, batch=3, num_heads=8,
+                         kv_num_heads=2, head_size=128, block_size=32 if fmt == "int4" else 16,
+                         past=np.array([40, 0, 300]), q_lens=np.ones(3, np.int32),
+                         q_dtype="bf16" if fmt == "fp8" else "f16", kv_format=fmt,
+                         kv_in_dtype="f32", num_splits=splits)
+    _both(w, splits)
+
+
 def test_decode_append_two_launches():
-    """New rows in another dtype than the query's take the two operations one
-    after the other: same results."""
-    w = workloads.custom("dapp_sep", 3301, batch=3, num_heads=8, kv_num_heads=2,
+    """fp32 queries with 16-bit new rows take the two operations one after the
+    other: same results."""
+    w = workloads.custom("dapp_sep", 3311, batch=3, num_heads=8, kv_num_heads=2,
                          head_size=128, block_size=16, past=np.array([40, 0, 300]),
-                         q_lens=np.ones(3, np.int32), q_dtype="f16", kv_format="int8",
-                         kv_in_dtype="f32", num_splits=1)
+                         q_lens=np.ones(3, np.int32), q_dtype="f32", kv_format="int8",
+                         kv_in_dtype="f16", num_splits=1)
     _both(w, 1)
+
+
+def test_decode_append_int4_long():
+    """The whole int4_long step (fp32 new rows, 128 chunks)."""
+    w = workloads.make("int4_long")
+    _both(w, w.num_splits)
 
 
 def test_decode_append_tiny_decode():
