@@ -74,3 +74,20 @@ def test_append_bytes(rotary):
         extra = 2 * T * w.num_heads * w.head_size * size[w.q_dtype]           # query read + written
         extra += T * 2 * (w.head_size // 2) * 4                               # cos and sin rows
     assert bench.append_bytes(w, T, rotary) == rows_in + codes_out + extra
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """The bench measures one GPU: asked for more, it exits with status 2 and
+    says so before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv,
+                       capture_output=True, text=True, timeout=60, cwd=root,
+                       env=dict(os.environ, **env))
+    assert p.returncode == 2
+    assert "one GPU only" in p.stderr
+    assert p.stdout == ""
